@@ -1,0 +1,190 @@
+/*
+ * attn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct fp64 CPU reference for the forward pass of
+ * multi-head scaled-dot-product attention.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load this library; the product path never does.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (the textbook definition, not the tiled algorithm):
+ *   For each batch b, head h and query row i,
+ *     J(i)   = { j : 0 <= j < L_b and (not causal or j <= i) }     (masked keys excluded)
+ *     s_j    = scale * sum_d q[i,d] k[j,d]                          for j in J(i)
+ *     m      = max_j s_j                                            (two-pass max shift)
+ *     e_j    = exp(s_j - m),  l = sum_j e_j
+ *     O[i,:] = sum_j e_j v[j,:] / l
+ *     lse[i] = m + ln l                                             (natural log)
+ *   and for an empty J(i):  O[i,:] = 0,  lse[i] = -inf.
+ *
+ * Sources (the pages on scaled dot-product attention):
+ *   - definition softmax(Q K^T / sqrt(d_k)) V and the masked_fill(mask == 0, -inf) step:
+ *     the hotelren.com page, ch.1 code and sec.2.1 formula and "PyTorch hand-written
+ *     implementation"; the qqiyuan.cn page, "original implementation" (fill -1e9) and
+ *     its pitfalls list (additive -10000 mask).  Excluding masked keys equals all three
+ *     fill conventions on every row that keeps at least one key.
+ *   - causal mask = attend only to the current and earlier positions: hotelren.com
+ *     sec.2.1 note 2; lshu.cn sec.3.1.  Read here as j <= i (top-left aligned).
+ *   - max-shifted softmax and log-sum-exp = max + log(sum exp(x - max)):
+ *     aicoding.csdn.net sec.2.2 ("numerical stability of softmax", chunked logsumexp).
+ *   - the fused method is numerically the same as the plain one: aicoding.csdn.net ch.1
+ *     table; lshu.cn sec.2.2.  So the oracle is the plain definition.
+ *
+ * Inputs are the stored bytes (fp32, fp16 or bf16); each is widened exactly to fp64 by
+ * the decoders below.  `scale` is the same value the GPU path receives (already rounded
+ * to float32 by the caller), widened.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+/* bfloat16 is the top half of an IEEE binary32 pattern. */
+static double dec_bf16(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+static double dec_f16(uint16_t h) {
+    int sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);            /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double dec(const void* base, int dtype, int64_t idx) {
+    if (dtype == OR_F32) {
+        float f;
+        memcpy(&f, (const char*)base + 4 * idx, 4);
+        return (double)f;
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)base + 2 * idx, 2);
+    return dtype == OR_F16 ? dec_f16(h) : dec_bf16(h);
+}
+
+static void decode_row(const void* base, int dtype, int64_t off, int D, double* out) {
+    for (int d = 0; d < D; ++d) out[d] = dec(base, dtype, off + d);
+}
+
+/* One query row (b, h, i).  Scratch: qrow[D], s[Nk]. */
+static void one_row(const void* q, const void* k, const void* v, int dtype, int H, int Nq,
+                    int Nk, int D, double scale, int causal, const int32_t* key_lens, int64_t row,
+                    double* o, double* lse, double* qrow, double* s, double* krow) {
+    int64_t bh = row / Nq;
+    int i = (int)(row % Nq);
+    int b = (int)(bh / H);
+    int64_t L = Nk;
+    if (key_lens) {
+        L = key_lens[b];
+        if (L < 0) L = 0;
+        if (L > Nk) L = Nk;
+    }
+    int64_t jend = L; /* J(i) = [0, jend) */
+    if (causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;
+
+    if (jend <= 0) {
+        for (int d = 0; d < D; ++d) o[d] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    decode_row(q, dtype, row * D, D, qrow);
+    int64_t kbase = bh * (int64_t)Nk * D;
+
+    /* logits */
+    for (int64_t j = 0; j < jend; ++j) {
+        decode_row(k, dtype, kbase + j * D, D, krow);
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += qrow[d] * krow[d];
+        s[j] = scale * acc;
+    }
+    /* pass 1: max */
+    double m = s[0];
+    for (int64_t j = 1; j < jend; ++j)
+        if (s[j] > m) m = s[j];
+    /* pass 2: shifted exponentials and their sum */
+    double l = 0.0;
+    for (int64_t j = 0; j < jend; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    /* weighted sum of values */
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < jend; ++j) {
+        decode_row(v, dtype, kbase + j * D, D, krow);
+        for (int d = 0; d < D; ++d) o[d] += s[j] * krow[d];
+    }
+    for (int d = 0; d < D; ++d) o[d] /= l;
+    *lse = m + log(l);
+}
+
+/*
+ * oracle_attn_rows -- reference attention on selected query rows.
+ *   q: [B,H,Nq,D], k, v: [B,H,Nk,D], contiguous, stored as `dtype` (0 fp32, 1 fp16, 2 bf16).
+ *   key_lens: int32[B] or NULL (every key valid); values are clamped to [0, Nk].
+ *   rows: flat row ids ((b*H + h)*Nq + i), or NULL for all B*H*Nq rows in order.
+ *   o: fp64 [nrows, D]; lse: fp64 [nrows].
+ *   nthreads <= 0 uses the OpenMP default.
+ * Returns 0, -1 on a bad argument, -2 if scratch memory cannot be allocated.
+ */
+int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int B, int H, int Nq,
+                     int Nk, int D, double scale, int causal, const int32_t* key_lens,
+                     const int64_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
+    if (!q || !k || !v || !o || !lse) return -1;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return -1;
+    int64_t total = (int64_t)B * H * Nq;
+    if (!rows) nrows = total;
+    for (int64_t r = 0; rows && r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return -1;
+    int nt = 1;
+#ifdef _OPENMP
+    nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#endif
+    (void)nthreads;
+    /* per-thread scratch: qrow[D], krow[D], s[Nk] */
+    size_t per = (size_t)2 * D + (size_t)Nk;
+    double* scratch = (double*)malloc(sizeof(double) * per * (size_t)nt);
+    if (!scratch) return -2;
+#pragma omp parallel num_threads(nt)
+    {
+        int t = 0;
+#ifdef _OPENMP
+        t = omp_get_thread_num();
+#endif
+        double* qrow = scratch + per * (size_t)t;
+        double* krow = qrow + D;
+        double* s = krow + D;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            one_row(q, k, v, dtype, H, Nq, Nk, D, scale, causal, key_lens, row, o + r * D, lse + r,
+                    qrow, s, krow);
+        }
+    }
+    free(scratch);
+    return 0;
+}
+
+/* Decoders exposed for the tests' checks of the widening itself. */
+double oracle_decode(const void* base, int dtype, int64_t idx) { return dec(base, dtype, idx); }
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

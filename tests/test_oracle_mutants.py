@@ -1,0 +1,61 @@
+"""Plant plausible mistakes in copies of the oracle source (CPU only) and check that the pins
+catch every one.  The real oracle is never modified: each mutant is a textual edit of a
+temporary copy of attn_oracle.c, built with the oracle's own build command."""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = [
+    ("dropped scale", "s[j] = scale * acc;", "s[j] = acc;"),
+    ("scale applied twice", "s[j] = scale * acc;", "s[j] = scale * scale * acc;"),
+    ("q.q instead of q.k", "acc += qrow[d] * krow[d];", "acc += qrow[d] * qrow[d];"),
+    ("wrong sign in the shift", "s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
+    ("no max shift", "if (s[j] > m) m = s[j];", "if (s[j] > m) m = m;"),
+    ("min instead of max", "if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    ("missing normalisation", "for (int d = 0; d < D; ++d) o[d] /= l;", ""),
+    ("log2 in the LSE", "*lse = m + log(l);", "*lse = m + log2(l);"),
+    ("LSE without the max", "*lse = m + log(l);", "*lse = log(l);"),
+    ("causal j < i", "jend = (int64_t)i + 1;", "jend = (int64_t)i;"),
+    ("causal ignored", "if (causal && jend > (int64_t)i + 1)", "if (0 && jend > (int64_t)i + 1)"),
+    ("key lengths ignored", "L = key_lens[b];", "L = Nk;"),
+    ("key length off by one", "L = key_lens[b];", "L = key_lens[b] - 1;"),
+    ("batch index from head", "int b = (int)(bh / H);", "int b = (int)(bh % H);"),
+    ("K/V base uses Nq", "int64_t kbase = bh * (int64_t)Nk * D;", "int64_t kbase = bh * (int64_t)Nq * D;"),
+    ("V rows reversed", "decode_row(v, dtype, kbase + j * D, D, krow);",
+     "decode_row(v, dtype, kbase + (jend - 1 - j) * D, D, krow);"),
+    ("V read from K", "decode_row(v, dtype, kbase + j * D, D, krow);",
+     "decode_row(k, dtype, kbase + j * D, D, krow);"),
+    ("empty row LSE 0", "*lse = -INFINITY;", "*lse = 0.0;"),
+    ("bf16 shift 15", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    ("fp16 bias off by one", "e - 25);", "e - 24);"),
+    ("fp16 subnormal scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("sum of unshifted exps", "l += s[j];", "l += s[j] * exp(m);"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(desc, old, new, source, tmp_path):
+    assert source.count(old) == 1, f"mutation anchor for {desc!r} must occur exactly once"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = oracle.build(str(src), str(tmp_path / "libmutant.so"))
+    impl = oracle.Oracle(lib)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(impl)
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            caught.append((pin.__name__, str(e)[:80]))
+            break
+    assert caught, f"no pin caught the planted mistake: {desc}"
+    os.remove(lib)
