@@ -1,0 +1,93 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused attention forward.
+ *
+ * Operation (multi-head scaled-dot-product attention, forward only).  For every batch b,
+ * head h and query row i:
+ *     O[b,h,i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:]  over the valid keys j ) V[b,h,:,:]
+ *     LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,h,j,:] )   over the same keys
+ * Sources: the definition softmax(Q K^T / sqrt(d_k)) V with an optional mask filled before the
+ * softmax (hotelren.com page on attention, ch.1 code and sec.2.1); the causal mask that lets a
+ * position see only itself and earlier positions (same page, sec.2.1; lshu.cn page, sec.3.1);
+ * the boolean padding mask where true means "may attend" (lshu.cn page, sec.5.2); the
+ * max-shifted log-sum-exp (aicoding.csdn.net page, sec.2.2); the fused tiled loop that never
+ * stores the score matrix (hotelren.com page, sec.4.1) and skips inactive key tiles (same
+ * page, ch.5); the fused-library call taking q, k, v in [b, h, s, d] with a causal flag and a
+ * softmax scale (aicoding.csdn.net page, ch.5).
+ *
+ * Valid keys of row i in batch b: j < L_b, and j <= i when causal (top-left aligned), with
+ * L_b = key_lens ? clamp(key_lens[b], 0, Nk) : Nk.  A row with no valid key gets O = 0 and
+ * LSE = -inf.  Masked keys are left out of the softmax (equal to filling with -inf, -1e9 or
+ * adding -10000 on every row that keeps a key).
+ *
+ * The library allocates nothing, keeps no pointer after returning, holds no mutable global
+ * state and is re-entrant.  No HIP header is needed to call it: the stream is passed as
+ * void* (a hipStream_t; NULL is the default stream).
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of q, k, v and o.  Scores, softmax state and accumulation are fp32 for all. */
+typedef enum {
+    ATTN_F32 = 0,  /* IEEE binary32 */
+    ATTN_F16 = 1,  /* IEEE binary16 */
+    ATTN_BF16 = 2  /* bfloat16 (top half of binary32) */
+} attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,     /* q, k, v, o or lse is NULL */
+    ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, or a size beyond the 32-bit limits below */
+    ATTN_ERR_HEAD_DIM = -3, /* D is not 64 or 128 */
+    ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype */
+    ATTN_ERR_SCALE = -5,    /* scale is not finite */
+    ATTN_ERR_FLAG = -6,     /* causal is not 0 or 1 */
+    ATTN_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
+    ATTN_ERR_ALIGN = -8     /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
+} attn_status;
+
+/*
+ * attn_fwd -- enqueue the fused attention forward on `stream` and return.
+ *
+ *   q        device, [B, H, Nq, D] row-major contiguous, `dtype`.
+ *   k, v     device, [B, H, Nk, D] row-major contiguous, `dtype`.
+ *   o        device, [B, H, Nq, D] row-major contiguous, `dtype` (written; rounded to nearest
+ *            even from the fp32 result).
+ *   lse      device, fp32 [B, H, Nq] (written): natural-log log-sum-exp of the scaled logits over
+ *            the valid keys.
+ *   B, H     batch and heads, >= 1.
+ *   Nq, Nk   query and key lengths, >= 1.  Any length is accepted (tails are masked inside the
+ *            kernel); Nk * D and Nq * D must stay below 2^29 elements per (b, h).
+ *   D        head dimension shared by q, k and v: 64 or 128.
+ *   scale    finite fp32 multiplier of the raw dot products (normally 1/sqrt(D)); it may be 0 or
+ *            negative.
+ *   causal   0 or 1.
+ *   key_lens NULL (all Nk keys valid) or device int32[B]; values outside [0, Nk] are clamped.
+ *   dtype    an attn_dtype.
+ *   stream   hipStream_t as void*, NULL for the default stream.
+ *
+ * Alignment: q, k, v, o and lse must be 16-byte aligned, key_lens 4-byte aligned.
+ * Ownership: every buffer belongs to the caller and must stay valid until the enqueued work
+ * has finished; outputs must not alias inputs.
+ * Errors: arguments are checked on the host before anything is enqueued; on any error the
+ * function returns a negative attn_status and writes nothing.  A launch failure reported by
+ * the runtime returns ATTN_ERR_LAUNCH.  Faults inside the kernel (e.g. a pointer that is not
+ * device memory of the stated size) surface on the stream, not here.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+             void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

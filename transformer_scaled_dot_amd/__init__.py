@@ -1,0 +1,17 @@
+"""MI355X (gfx950) fused multi-head scaled-dot-product attention forward.
+
+    from transformer_scaled_dot_amd import fwd
+    o, lse = fwd(q, k, v, causal=True)
+
+The computation lives in libattn_fwd.so (hand-written HIP kernels behind the C ABI declared in
+include/attn_fwd.h); `binding` marshals arguments to it.  `inputs` is the seeded generator of
+synthetic workloads.  Importing the package loads nothing; the library is loaded on first use.
+"""
+
+
+def __getattr__(name):
+    if name in ("fwd", "attn_fwd", "attn_status_str", "AttnError", "load_library"):
+        from . import binding
+
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,134 @@
+"""Python binding of the C ABI in include/attn_fwd.h (argument marshalling only).
+
+`attn_fwd` and `attn_status_str` mirror the C entry points one to one (raw device pointers,
+sizes, a stream handle).  `fwd` is the tensor-level convenience: it checks the tensors on the
+host, allocates O and LSE with torch on the current stream and calls `attn_fwd`.  Every step of
+the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
+module raises instead of computing anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_fwd.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_OK = 0
+STATUS = {
+    0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
+    -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_FLAG", -7: "ATTN_ERR_LAUNCH",
+    -8: "ATTN_ERR_ALIGN",
+}
+EXPORTS = ("attn_fwd", "attn_status_str")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"attn_fwd failed: {STATUS.get(status, status)} ({attn_status_str(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn_fwd.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m transformer_scaled_dot_amd.build`"
+                           " (there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+    ]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, stream) -> int:
+    """The C entry point: device pointers as ints (or None), sizes, dtype code, stream handle."""
+    return load_library().attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens,
+                                   dtype, stream)
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None, out=None,
+        lse=None, stream=None):
+    """O, LSE = attention(q, k, v).  q: [B,H,Nq,D]; k, v: [B,H,Nk,D]; all contiguous CUDA tensors
+    of one dtype; key_lens: int32 [B] on the same device or None.  scale defaults to 1/sqrt(D).
+    Returns O (q's dtype, [B,H,Nq,D]) and LSE (float32, [B,H,Nq])."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, D]")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k and v must be on one device")
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, D) or tuple(v.shape) != (B, H, Nk, D):
+        raise ValueError(f"k and v must be [B={B}, H={H}, Nk, D={D}]; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if D not in (64, 128):
+        raise ValueError(f"head dimension must be 64 or 128, got {D}")
+    if min(B, H, Nq, Nk) < 1:
+        raise ValueError("B, H, Nq and Nk must be >= 1")
+    code = dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if not math.isfinite(scale):
+        raise ValueError("scale must be finite")
+    kl_ptr = None
+    if key_lens is not None:
+        if (not isinstance(key_lens, torch.Tensor) or key_lens.dtype != torch.int32
+                or key_lens.device != q.device or tuple(key_lens.shape) != (B,)
+                or not key_lens.is_contiguous()):
+            raise ValueError("key_lens must be a contiguous int32 tensor [B] on q's device")
+        kl_ptr = key_lens.data_ptr()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Nq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                  B, H, Nq, Nk, D, float(scale), int(bool(causal)), kl_ptr, code, handle)
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return out, lse

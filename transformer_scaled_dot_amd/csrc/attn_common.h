@@ -1,0 +1,48 @@
+// attn_common.h -- types shared by the HIP kernels and their host launcher (HIP path only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Everything a kernel needs about one call.  Sizes are validated on the host.
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* key_lens;  // device int32[B] or nullptr
+    int B, H, Nq, Nk;
+    int n_qtiles;      // ceil(Nq / BM) for the kernel's BM
+    int n_blocks;      // n_qtiles * H * B
+    float scale_log2;  // |scale| * log2(e): logits are handled in base-2 units
+    int negate_q;      // scale < 0: the sign is moved onto Q (an exact bit flip)
+    int causal;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).
+// Renumber them so that each XCD walks one contiguous range of the logical order: the
+// q-tiles of one (b, h) then run on the same XCD at about the same time and share the K/V
+// stream through that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    if ((n & 7) != 0) return bid;
+    return (bid & 7) * (n >> 3) + (bid >> 3);
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* key_lens, int b, int Nk) {
+    if (!key_lens) return Nk;
+    int L = key_lens[b];
+    return L < 0 ? 0 : (L > Nk ? Nk : L);
+}
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+}  // namespace attn
+
+// Launchers, one per kernel family (defined in their .hip files).
+hipError_t attn_launch_mfma(const attn::Params& p, int dtype, int D, hipStream_t stream);
+hipError_t attn_launch_f32(const attn::Params& p, int D, hipStream_t stream);
+int attn_mfma_block_m();
+int attn_f32_block_m();

@@ -1,0 +1,64 @@
+// attn_fwd_api.hip -- the C ABI: argument checks, kernel choice, launch on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include <attn_fwd.h>
+#include "attn_common.h"
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Nq, int Nk, int D, float scale, int causal,
+                        const int32_t* key_lens, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+    if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+    if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) != 0 ||
+        ((uintptr_t)key_lens & 3) != 0)
+        return ATTN_ERR_ALIGN;
+    // Per-(b, h) slices are addressed with 32-bit byte offsets (4-byte elements at most).
+    if ((int64_t)Nq * D >= ((int64_t)1 << 29) || (int64_t)Nk * D >= ((int64_t)1 << 29))
+        return ATTN_ERR_SHAPE;
+
+    const int bm = dtype == ATTN_F32 ? attn_f32_block_m() : attn_mfma_block_m();
+    const int64_t n_qtiles = ((int64_t)Nq + bm - 1) / bm;
+    const int64_t n_blocks = n_qtiles * H * B;
+    if (n_blocks > INT32_MAX) return ATTN_ERR_SHAPE;
+
+    attn::Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.key_lens = key_lens;
+    p.B = B;
+    p.H = H;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.n_qtiles = (int)n_qtiles;
+    p.n_blocks = (int)n_blocks;
+    p.scale_log2 = (float)(fabs((double)scale) * 1.4426950408889634074);
+    p.negate_q = scale < 0.f;
+    p.causal = causal;
+
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = dtype == ATTN_F32 ? attn_launch_f32(p, D, s) : attn_launch_mfma(p, dtype, D, s);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer (q, k, v, o, lse) is NULL";
+        case ATTN_ERR_SHAPE: return "B, H, Nq, Nk must be >= 1 and each (b, h) slice below 2^29 elements";
+        case ATTN_ERR_HEAD_DIM: return "head dimension D must be 64 or 128";
+        case ATTN_ERR_DTYPE: return "dtype must be ATTN_F32, ATTN_F16 or ATTN_BF16";
+        case ATTN_ERR_SCALE: return "scale must be finite";
+        case ATTN_ERR_FLAG: return "causal must be 0 or 1";
+        case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+        case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned, key_lens 4-byte aligned";
+        default: return "unknown status";
+    }
+}
