@@ -1,0 +1,257 @@
+"""Benchmark: fused attention forward on one MI355X, long-context causal workload by default.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
+resident in HBM).  W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation, timed with HIP events recorded on the stream the kernel is launched on.
+Prints ONE JSON line on stdout (everything else goes to stderr).
+
+The CPU baseline times the fp64 oracle, untouched, on a bounded random sample of the same
+workload's rows and scales it to the same unit; the same rows are compared with the GPU
+output.  Only this leg loads the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·D, causal halved) and % of bf16 MFMA peak"
+# MI355X published dense peaks (256 CUs at 2.4 GHz).
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "transformer_scaled_dot_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/<workload>_traffic.md), if
+    they were taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash:
+        return None
+    return float(m_bytes.group(1))
+
+
+def algorithmic_bytes(w) -> float:
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    return eb * (2 * w.B * w.H * w.Nq * w.D + 2 * w.B * w.H * w.Nk * w.D) + 4 * w.B * w.H * w.Nq
+
+
+def row_pairs(w, rows, key_lens):
+    """Number of (query, valid key) pairs of each flat row id."""
+    import numpy as np
+
+    i = rows % w.Nq
+    b = rows // (w.H * w.Nq)
+    L = np.full(rows.shape, w.Nk, dtype=np.int64) if key_lens is None else \
+        np.clip(key_lens.astype(np.int64), 0, w.Nk)[b]
+    return np.minimum(L, i + 1) if w.causal else L
+
+
+def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
+    """Time the oracle on a random sample of rows (pilot run, then ~target_s of work)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    impl = oracle.default()
+    cores = impl.max_threads()
+    rng = np.random.default_rng(seed)
+    total = w.B * w.H * w.Nq
+    args = (x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), w.causal, x["key_lens"])
+
+    # Size the sample from a timed pilot, growing it until it covers at least half the target.
+    n = 256
+    while True:
+        n = min(n, total)
+        rows = np.sort(rng.choice(total, size=n, replace=False)) if n < total else np.arange(total)
+        t0 = time.perf_counter()
+        ro, rl = impl.attn_rows(*args, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= total:
+            break
+        n = int(n * min(64.0, max(2.0, target_s / max(dt, 1e-3))))
+    flops = 4.0 * w.D * float(row_pairs(w, rows, x["key_lens"]).sum())
+
+    D = w.D
+    o = o_dev.detach().reshape(-1, D)[torch.from_numpy(rows).to(o_dev.device)].double().cpu().numpy()
+    lse = lse_dev.detach().reshape(-1)[torch.from_numpy(rows).to(o_dev.device)].double().cpu().numpy()
+    fin = np.isfinite(rl)
+    err_o = float(np.max(np.abs(o - ro)))
+    err_l = float(np.max(np.abs(lse[fin] - rl[fin]))) if fin.any() else 0.0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{rows.size} random query rows of the same workload (seed {seed}), fp64 oracle "
+                  f"with {cores} OpenMP threads, {dt:.2f} s; flops counted as 4*D per valid "
+                  f"(query, key) pair, as in the metric",
+        "seconds": dt,
+        "sample_max_abs_err_o": err_o,
+        "sample_max_abs_err_lse": err_l,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(reference dispatch for HBM byte counters)")
+    a = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE={world}); heads shard across GPUs with no communication, but no "
+              f"multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_scaled_dot_amd import binding, inputs
+
+    name = a.workload or inputs.BENCH_WORKLOAD
+    w = inputs.WORKLOADS[name]
+    log(f"[bench] workload {name}: generating inputs")
+    t0 = time.perf_counter()
+    x = inputs.make_inputs(w)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def to_dev(arr):
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+        if w.dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(dev)
+
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    kl = None if x["key_lens"] is None else torch.from_numpy(x["key_lens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = float(x["scale"])
+
+    def step():
+        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warm-up done ({a.warmup} steps)")
+
+    # Timed region: K steps; an event pair around every launch on the launch stream.
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(a.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    region_ms = region0.elapsed_time(region1)
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = region_ms / a.steps
+    log(f"[bench] {a.steps} steps: region {region_ms:.3f} ms, {ms_per_step:.4f} ms/step, "
+        f"avg launch {avg_launch_ms:.4f} ms (min {min(launch_ms):.4f}), wall {wall:.3f} s")
+
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        log(f"[bench] calibration copy: {a.calib_copy_mib} MiB read + {a.calib_copy_mib} MiB written")
+        del src, dst
+
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(name, src_hash)
+    abytes = algorithmic_bytes(w)
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "key_padding": w.padded, "seed": x["seed"],
+                   "parallelism": "none (1 GPU)"},
+        "pct_of_peak": 100.0 * value / peak,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic},
+        "avg_launch_ms": avg_launch_ms,
+        "algorithmic_bytes": abytes,
+        "algorithmic_gbs": abytes / (avg_launch_ms * 1e-3) / 1e9,
+        "kernel_source_sha256": src_hash,
+        "input_sha256": inputs.input_hashes(x),
+    }
+    if not a.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on a sample (~{a.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(w, x, o, lse, a.cpu_seconds)
+        cb = result["cpu_baseline"]
+        log(f"[bench] cpu baseline {cb['value'] * 1e3:.3f} GFLOP/s on {cb['cores']} threads; "
+            f"sample max|dO|={cb['sample_max_abs_err_o']:.3e} max|dLSE|={cb['sample_max_abs_err_lse']:.3e}")
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
