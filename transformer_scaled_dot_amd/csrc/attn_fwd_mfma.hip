@@ -5,18 +5,23 @@
 // load only the K/V tiles a Q tile can see) laid out for CDNA4:
 //
 //   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
-//   * K/V tiles of 64 keys go HBM -> registers -> LDS (double buffered, one barrier per tile);
+//   * K/V tiles of 64 keys go HBM -> LDS by the buffer-load-to-LDS path (no registers, no LDS
+//     store instructions), double buffered, one barrier per tile; the next tile's loads are in
+//     flight while the current one is computed;
 //   * both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation, arranged so
 //     that a lane always holds one query row:
-//        S^T = K Q^T   (A = K tile from LDS, B = Q^T kept in registers for the whole loop)
-//        O^T = V^T P^T (A = V^T tile from LDS, B = P^T taken straight from the S^T accumulator)
+//        S^T = K Q^T   (A = K tile read from LDS, B = Q^T kept in registers for the whole loop)
+//        O^T = V^T P^T (A = V^T read from the row-major V tile with the LDS transpose read,
+//                       B = P^T taken straight from the S^T accumulator)
 //     The 32x32 accumulator gives lane l the column l%32 (the query) and 16 rows (keys); the K
 //     rows are fed to the MFMA with bits 2 and 3 of the row index swapped, which makes each
 //     lane's 8-register halves hold 8 consecutive keys -- exactly the B-operand layout of the
 //     next MFMA, so P never moves between lanes;
-//   * the softmax runs per lane in base-2 units (logit * scale * log2 e) with fp32 running
-//     max and sum; the two lanes that share a query row swap maxima once per tile and sums
-//     once at the end;
+//   * the softmax runs per lane in base-2 units (logit * scale * log2 e) with an fp32 running
+//     max and sum.  The two lanes that share a query row swap maxima once per tile.  The
+//     reference max is raised (and O, l rescaled) only when a row's tile max exceeds it by more
+//     than 2^8; otherwise P is formed against the stale reference, which leaves O / l and
+//     ln 2 (m + log2 l) unchanged;
 //   * tiles beyond a row's last valid key are never loaded (causal and key padding); masks
 //     are evaluated only on the tiles that straddle a boundary.
 #include "attn_common.h"
@@ -27,6 +32,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 template <typename T>
 struct Mfma;
@@ -50,56 +60,48 @@ struct Mfma<_Float16> {
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 constexpr int BM = 128;  // query rows per workgroup
 constexpr int BN = 64;   // keys per K/V tile
+constexpr float kRescaleGap = 8.0f;             // base-2 units: P stays below 2^8
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
 
 // Row permutation of the K operand: swap bits 2 and 3 of a 0..31 row index (an involution).
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-// XOR swizzles of the 16-byte chunk index, chosen so that the 32 lanes of a half-wave that
-// read one MFMA operand (one chunk column, 32 different rows) hit distinct LDS banks whether
-// the LDS serves 8 or 16 lanes of a 128-bit read per clock.
+// K tile in LDS: row-major [BN][D], 16-byte chunk c of row `row` stored at chunk c ^ kswz(...).
+// The 32 lanes of a half-wave read one chunk column of 32 rows (rows swap23(r)); the XOR puts
+// them on distinct banks whether the LDS serves 8 or 16 lanes of a 128-bit read per clock.
 template <int D>
-__device__ __forceinline__ int kswz(int r) {  // r: lane row 0..31 of the A operand
+__device__ __forceinline__ int kswz_lane(int r) {  // r: lane row 0..31 of the A operand
     return D == 128 ? (r & 15) : (((r >> 1) & 7) ^ ((r & 1) << 2));
 }
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
+template <int D>
+__device__ __forceinline__ int kswz_row(int row) { return kswz_lane<D>(swap23(row & 31)); }
 
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
-}
-
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::vec8 to_vec8(u32x4_t x) {
-    return __builtin_bit_cast(typename Mfma<T>::vec8, x);
-}
-
-// 8 fp32 values -> 8 x T, round to nearest even.
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::vec8 cvt8(const f32x16_t& s, int base) {
-    typename Mfma<T>::vec8 r;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (T)s[base + i];
-    return r;
-}
-
-template <typename T>
-__device__ __forceinline__ unsigned short bits16(T x) {
-    return __builtin_bit_cast(unsigned short, x);
+// V tile in LDS: row-major [BN][D].  The transpose read takes 4 consecutive rows x 32 bytes
+// per 16 lanes; XOR-ing the chunk index with a function of (row mod 4) spreads the 32 lanes of
+// a half-wave over all banks.
+template <int D>
+__device__ __forceinline__ int vswz_row(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 template <typename T, int D>
 __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
+    // The body is device code only: its LDS address-space casts mean nothing to the host pass,
+    // which needs just the kernel's signature to emit the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
     using M = Mfma<T>;
-    constexpr int NCH = D / 8;             // 16-byte chunks per K/V row
-    constexpr int KSTEPS = D / 16;         // k-steps of S^T = K Q^T
-    constexpr int DT = D / 32;             // 32-row tiles of O^T
-    constexpr int KT = BN / 32;            // 32-key tiles of S^T
-    constexpr int K_LOADS = BN * NCH / NT; // 16-byte K chunks per thread per tile
-    constexpr int V_ITEMS = (BN / 2) * NCH / NT;  // (key pair, chunk) items per thread per tile
-    constexpr int TILE_BYTES = BN * D * 2;
-    static_assert(K_LOADS >= 1 && V_ITEMS >= 1, "tile too small for the workgroup");
+    using vec8 = typename M::vec8;
+    constexpr int NCH = D / 8;              // 16-byte chunks per K/V row
+    constexpr int KSTEPS = D / 16;          // k-steps of S^T = K Q^T
+    constexpr int DT = D / 32;              // 32-row tiles of O^T
+    constexpr int KT = BN / 32;             // 32-key tiles of S^T
+    constexpr int CPT = BN * NCH / NT;      // 16-byte chunks per thread per tile (K or V)
+    constexpr int TILE = BN * D * 2;        // bytes of one K or V tile
+    constexpr int STAGE = 2 * TILE;         // K tile then V tile
+    static_assert(CPT >= 1, "tile too small for the workgroup");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TILE_BYTES];  // K[2], V^T[2]
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * STAGE];
+    lds_u8* const smem = (lds_u8*)smem_raw;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -122,113 +124,108 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const T* qg = (const T*)p.q + (size_t)bh * p.Nq * D;
     const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
     const T* vg = (const T*)p.v + (size_t)bh * p.Nk * D;
-    // Out-of-range buffer reads return 0: rows past Nq, and keys past the valid length.
-    const __amdgpu_buffer_rsrc_t qrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, p.Nq * D * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, kv_valid * D * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, kv_valid * D * 2, kBufferWord3);
 
-    // Q^T operand: lane (r, g) holds Q[qi][16 ks + 8 g .. +7] for every k-step.
-    typename M::vec8 qf[KSTEPS];
+    // Q^T operand: lane (r, g) holds Q[qi][16 ks + 8 g .. +7]; rows past Nq read as 0.
+    vec8 qf[KSTEPS];
+    {
+        const __amdgpu_buffer_rsrc_t qrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, p.Nq * D * 2, kBufferWord3);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-        u32x4_t x = buf_load16(qrs, (qi * D + 16 * ks + 8 * g) * 2);
-        if (p.negate_q) x ^= 0x80008000u;
-        qf[ks] = to_vec8<T>(x);
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (qi * D + 16 * ks + 8 * g) * 2, 0, 0);
+            if (p.negate_q) x ^= 0x80008000u;
+            qf[ks] = __builtin_bit_cast(vec8, x);
+        }
     }
 
-    u32x4_t kreg[K_LOADS];
-    u32x4_t vreg[2 * V_ITEMS];
-
-    auto load_tile = [&](int j0) {
+    // Per-lane byte offsets of this thread's tile loads: slot (i*NT + tid) of a tile holds the
+    // global 16-byte chunk (row, chunk ^ swizzle(row)).
+    int koff[CPT], voff[CPT];
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / NCH, ch = c % NCH;
-            kreg[i] = buf_load16(krs, ((j0 + row) * D + ch * 8) * 2);
+    for (int i = 0; i < CPT; ++i) {
+        const int s = i * NT + tid;
+        const int row = s / NCH, phys = s % NCH;
+        koff[i] = (row * D + (phys ^ kswz_row<D>(row)) * 8) * 2;
+        voff[i] = (row * D + (phys ^ vswz_row<D>(row)) * 8) * 2;
+    }
+    auto issue_tile = [&](const int tile, const int stage) {
+        const int j0 = tile * BN;
+        // Keys at or past the valid length fall outside the buffer and arrive as zeros.
+        const int bytes = (kv_valid - j0) * D * 2;
+        const __amdgpu_buffer_rsrc_t krs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* kd = smem + stage * STAGE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kd, 16, koff[i], 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < V_ITEMS; ++i) {
-            const int c = tid + NT * i;
-            const int pr = c % 32, dc = c / 32;
-            vreg[2 * i] = buf_load16(vrs, ((j0 + 2 * pr) * D + dc * 8) * 2);
-            vreg[2 * i + 1] = buf_load16(vrs, ((j0 + 2 * pr + 1) * D + dc * 8) * 2);
-        }
-    };
-
-    auto store_tile = [&](int buf) {
-        unsigned char* kl = smem + buf * TILE_BYTES;
-        unsigned char* vl = smem + (2 + buf) * TILE_BYTES;
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int c = tid + NT * i;
-            const int row = c / NCH, ch = c % NCH;
-            const int phys = ch ^ kswz<D>(swap23(row & 31));
-            *(u32x4_t*)(kl + row * (D * 2) + phys * 16) = kreg[i];
-        }
-        // V is stored transposed, V^T[d][key], so the O^T operand reads 8 consecutive keys.
-#pragma unroll
-        for (int i = 0; i < V_ITEMS; ++i) {
-            const int c = tid + NT * i;
-            const int pr = c % 32, dc = c / 32;
-            const u32x4_t x0 = vreg[2 * i], x1 = vreg[2 * i + 1];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const unsigned a = x0[e >> 1], bb = x1[e >> 1];
-                const unsigned w = (e & 1) ? ((a >> 16) | (bb & 0xffff0000u))
-                                           : ((a & 0xffffu) | (bb << 16));
-                const int d = dc * 8 + e;
-                const int phys = (pr >> 2) ^ vswz(d);
-                *(unsigned*)(vl + d * (BN * 2) + phys * 16 + (pr & 3) * 4) = w;
-            }
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* vd = smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vd, 16, voff[i], 0, 0, 0);
         }
     };
+
+    // Per-lane LDS read offsets.
+    // K (A operand of S^T): row swap23(r) (+32 kt), chunk (2 ks + g) ^ kswz.
+    int kaddr[KSTEPS];
+    {
+        const int kr = kswz_lane<D>(r);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) kaddr[ks] = swap23(r) * (D * 2) + (((2 * ks + g) ^ kr) * 16);
+    }
+    // V^T (A operand of O^T) by transpose reads: within each 16-lane group (s = lane & 15), lane
+    // s names 8 bytes of V row (16 h16 + 8 g + 4 u + s/4) at columns 32 dt + 16 G + 4 (s & 3);
+    // lane s then receives column 32 dt + 16 G + s of those 4 rows.
+    int vaddr[DT];
+    {
+        const int s = lane & 15, G1 = (lane >> 4) & 1;
+        const int fl = vswz_row<D>(s >> 2) >> 2;  // rows of one read differ only in their low 2 bits
+        const int base = (8 * g + (s >> 2)) * (D * 2) + (2 * G1 + ((s & 3) >> 1)) * 16 + 8 * (s & 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vaddr[dt] = base + 64 * (dt ^ fl);
+    }
 
     f32x16_t oacc[DT];
 #pragma unroll
     for (int t = 0; t < DT; ++t) oacc[t] = f32x16_t{};
-    float m_run = -INFINITY;  // running max of this row, base-2 units
+    float m_ref = -INFINITY;  // reference max of this row (base-2 units)
     float l_run = 0.f;        // this lane's share of the running sum
-
     const float c2 = p.scale_log2;
-    const int kswz_r = kswz<D>(r);
-    const int vswz_r = vswz(r);
     const bool wave_has_rows = qw0 < p.Nq;
 
-    if (n_tiles > 0) load_tile(0);
-    for (int it = 0; it < n_tiles; ++it) {
-        const int buf = it & 1;
-        store_tile(buf);
+    auto do_tile = [&](const int it, const int stage) {
+        // Tile `it` is in LDS once every wave's loads have landed; the barrier also retires all
+        // reads of the other stage, which the next loads overwrite.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (it + 1 < n_tiles) load_tile((it + 1) * BN);
+        if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
 
         const int j0 = it * BN;
-        const bool active = wave_has_rows && !(p.causal && j0 > qw0 + 31);
-        if (!active) continue;
-
-        const unsigned char* kl = smem + buf * TILE_BYTES;
-        const unsigned char* vl = smem + (2 + buf) * TILE_BYTES;
+        if (!wave_has_rows || (p.causal && j0 > qw0 + 31)) return;  // nothing visible here
+        const lds_u8* kb = smem + stage * STAGE;
+        const lds_u8* vb = kb + TILE;
 
         // ---- S^T = K Q^T: 32 keys x 32 queries per accumulator
         f32x16_t s[KT];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             s[kt] = f32x16_t{};
-            const unsigned char* krow = kl + (swap23(r) + 32 * kt) * (D * 2);
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const u32x4_t a = *(const u32x4_t*)(krow + (((2 * ks + g) ^ kswz_r) * 16));
-                s[kt] = M::mma(to_vec8<T>(a), qf[ks], s[kt]);
+                const u32x4_t a = *(const lds_u32x4*)(kb + kaddr[ks] + kt * 32 * D * 2);
+                s[kt] = M::mma(__builtin_bit_cast(vec8, a), qf[ks], s[kt]);
             }
         }
 
         // ---- online softmax.  Register i of s[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.
         const bool need_mask = (j0 + BN > kv_valid) || (p.causal && j0 + BN - 1 > qw0);
-        float mt = -INFINITY;
+        float mt;
         if (need_mask) {
             const int lim = p.causal ? min(kv_valid, qi + 1) : kv_valid;
+            mt = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -239,53 +236,71 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
                     mt = fmaxf(mt, t);
                 }
         } else {
-            float mx = -INFINITY;
+            float mx = s[0][0];
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+                for (int i = (kt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
             mt = mx * c2;
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float ls = 0.f;
-        if (need_mask) {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
-                    s[kt][i] = e;
-                    ls += e;
-                }
-        } else {
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -m_use));
-                    s[kt][i] = e;
-                    ls += e;
-                }
+        {
+            // both halves of the wave hold one row: take the max across lanes l and l ^ 32
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mt),
+                                                             __builtin_bit_cast(unsigned, mt), false, false);
+            mt = fmaxf(__builtin_bit_cast(float, (unsigned)sw[0]), __builtin_bit_cast(float, (unsigned)sw[1]));
         }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
+        if (__any(mt > m_ref + kRescaleGap)) {
+            const float m_new = fmaxf(m_ref, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - (m_new == -INFINITY ? 0.f : m_new));
+            m_ref = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+            for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
+        // ---- P = 2^(t - m): fp32 row sum, rounded to T for the MFMA
+        vec8 pb[BN / 16];
+#pragma unroll
+        for (int h16 = 0; h16 < BN / 16; ++h16) {
+            const int kt = h16 >> 1, base = 8 * (h16 & 1);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float x0 = s[kt][base + e], x1 = s[kt][base + e + 1];
+                if (need_mask) {
+                    x0 = __builtin_amdgcn_exp2f(x0 - m_use);
+                    x1 = __builtin_amdgcn_exp2f(x1 - m_use);
+                } else {
+                    x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c2, -m_use));
+                    x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c2, -m_use));
+                }
+                pb[h16][e] = (T)x0;
+                pb[h16][e + 1] = (T)x1;
+                l_run += x0 + x1;
+            }
+        }
 
         // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
         for (int h16 = 0; h16 < BN / 16; ++h16) {
-            const typename M::vec8 pb = cvt8<T>(s[h16 >> 1], 8 * (h16 & 1));
-            const int vch = (2 * h16 + g) ^ vswz_r;
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
-                const u32x4_t a = *(const u32x4_t*)(vl + (32 * t + r) * (BN * 2) + vch * 16);
-                oacc[t] = M::mma(to_vec8<T>(a), pb, oacc[t]);
+                const lds_u8* a0 = vb + vaddr[t] + (16 * h16) * (D * 2);
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 4 * D * 2));
+                const vec8 a = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0],
+                                                                 __builtin_bit_cast(u32x2_t, lo)[1],
+                                                                 __builtin_bit_cast(u32x2_t, hi)[0],
+                                                                 __builtin_bit_cast(u32x2_t, hi)[1]});
+                oacc[t] = M::mma(a, pb[h16], oacc[t]);
             }
         }
+    };
+
+    if (n_tiles > 0) issue_tile(0, 0);
+    for (int it = 0; it < n_tiles; it += 2) {
+        do_tile(it, 0);
+        if (it + 1 < n_tiles) do_tile(it + 1, 1);
     }
 
     // ---- epilogue: O = O / l (rounded to T), LSE = ln 2 * (m + log2 l)
@@ -298,17 +313,18 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 // accumulator registers 4a..4a+3 hold O[qi][32 t + 8 a + 4 g + 0..3]
-                const unsigned w0 = bits16((T)(oacc[t][4 * a + 0] * inv)) |
-                                    ((unsigned)bits16((T)(oacc[t][4 * a + 1] * inv)) << 16);
-                const unsigned w1 = bits16((T)(oacc[t][4 * a + 2] * inv)) |
-                                    ((unsigned)bits16((T)(oacc[t][4 * a + 3] * inv)) << 16);
-                uint2* dst = (uint2*)(og + 32 * t + 8 * a + 4 * g);
-                *dst = make_uint2(w0, w1);
+                u32x2_t w;
+                w[0] = (unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 0] * inv)) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 1] * inv)) << 16);
+                w[1] = (unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 2] * inv)) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 3] * inv)) << 16);
+                *(u32x2_t*)(og + 32 * t + 8 * a + 4 * g) = w;
             }
         if (g == 0)
             p.lse[(size_t)bh * p.Nq + qi] =
-                l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * attn::kLn2 : -INFINITY;
+                l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * attn::kLn2 : -INFINITY;
     }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <typename T, int D>
