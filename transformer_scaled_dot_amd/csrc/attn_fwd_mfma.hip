@@ -104,7 +104,9 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     lds_u8* const smem = (lds_u8*)smem_raw;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    // the wave index is the same on every lane: keep it (and all per-wave decisions) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
     const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks);
@@ -260,23 +262,26 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
 
         // ---- P = 2^(t - m): fp32 row sum, rounded to T for the MFMA
+        if (need_mask) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kt][i] = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -m_use));
+        }
         vec8 pb[BN / 16];
 #pragma unroll
         for (int h16 = 0; h16 < BN / 16; ++h16) {
             const int kt = h16 >> 1, base = 8 * (h16 & 1);
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                float x0 = s[kt][base + e], x1 = s[kt][base + e + 1];
-                if (need_mask) {
-                    x0 = __builtin_amdgcn_exp2f(x0 - m_use);
-                    x1 = __builtin_amdgcn_exp2f(x1 - m_use);
-                } else {
-                    x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x0, c2, -m_use));
-                    x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x1, c2, -m_use));
-                }
-                pb[h16][e] = (T)x0;
-                pb[h16][e + 1] = (T)x1;
-                l_run += x0 + x1;
+            for (int e = 0; e < 8; ++e) {
+                pb[h16][e] = (T)s[kt][base + e];
+                l_run += s[kt][base + e];
             }
         }
 
