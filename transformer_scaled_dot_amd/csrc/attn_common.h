@@ -17,7 +17,7 @@ struct Params {
     int B, H, Nq, Nk;
     int n_qtiles;      // ceil(Nq / BM) for the kernel's BM
     int n_blocks;      // n_qtiles * H * B
-    float scale_log2;  // |scale| * log2(e): logits are handled in base-2 units
+    float scale_log2;  // max(|scale| * log2(e), 1e-30): logits are handled in base-2 units
     int negate_q;      // scale < 0: the sign is moved onto Q (an exact bit flip)
     int causal;
 };

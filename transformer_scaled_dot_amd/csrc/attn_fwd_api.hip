@@ -39,7 +39,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.Nk = Nk;
     p.n_qtiles = (int)n_qtiles;
     p.n_blocks = (int)n_blocks;
-    p.scale_log2 = (float)(fabs((double)scale) * 1.4426950408889634074);
+    // Logits are handled in base-2 units.  The kernels need a strictly positive multiplier (a
+    // masked logit is -inf and must stay -inf after scaling): a zero scale runs as 1e-30, which
+    // still gives every weight exactly 1 for raw dot products below 2^70 in magnitude
+    // (2^(1e-30 x) rounds to 1 in fp32 there).
+    p.scale_log2 = (float)fmax(fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.f;
     p.causal = causal;
 
