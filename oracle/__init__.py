@@ -37,11 +37,11 @@ class Oracle:
 
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
-        lib.oracle_attn_rows.restype = ctypes.c_int
-        lib.oracle_attn_rows.argtypes = [
+        lib.oracle_attn_rows_window.restype = ctypes.c_int
+        lib.oracle_attn_rows_window.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.oracle_decode.restype = ctypes.c_double
@@ -52,12 +52,13 @@ class Oracle:
         self.path = path
 
     def attn_rows(self, q, k, v, dtype: str, scale, causal: bool = False, key_lens=None,
-                  rows=None, nthreads: int = 0):
+                  rows=None, nthreads: int = 0, window=None):
         """Reference O (fp64 [n, D]) and LSE (fp64 [n]) for flat row ids ((b*H+h)*Nq+i).
 
         q: [B,H,Nq,D]; k, v: [B,H,Nk,D] in storage form (bf16 as uint16 bits).
         `scale` is used exactly as given (pass the float32 value the GPU path receives).
-        rows=None computes every row in order.
+        rows=None computes every row in order.  window=w keeps only keys with |i - j| <= w
+        (None: no window).
         """
         q = _as_storage(q, dtype)
         k = _as_storage(k, dtype)
@@ -79,18 +80,21 @@ class Oracle:
             n = r.size
         o = np.empty((n, D), dtype=np.float64)
         lse = np.empty(n, dtype=np.float64)
-        rc = self.lib.oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), _CODES[dtype], B, H, Nq, Nk,
-                                       D, float(scale), int(bool(causal)), _ptr(kl), _ptr(r), n,
-                                       _ptr(o), _ptr(lse), int(nthreads))
+        w = -1 if window is None else int(window)
+        if w < -1:
+            raise ValueError("window must be None or >= 0")
+        rc = self.lib.oracle_attn_rows_window(_ptr(q), _ptr(k), _ptr(v), _CODES[dtype], B, H, Nq,
+                                              Nk, D, float(scale), int(bool(causal)), w, _ptr(kl),
+                                              _ptr(r), n, _ptr(o), _ptr(lse), int(nthreads))
         if rc != 0:
             raise ValueError(f"oracle_attn_rows failed with {rc}")
         return o, lse
 
     def attn(self, q, k, v, dtype: str, scale, causal: bool = False, key_lens=None,
-             nthreads: int = 0):
+             nthreads: int = 0, window=None):
         """Reference O (fp64 [B,H,Nq,D]) and LSE (fp64 [B,H,Nq]) for every row."""
         B, H, Nq, D = q.shape
-        o, lse = self.attn_rows(q, k, v, dtype, scale, causal, key_lens, None, nthreads)
+        o, lse = self.attn_rows(q, k, v, dtype, scale, causal, key_lens, None, nthreads, window)
         return o.reshape(B, H, Nq, D), lse.reshape(B, H, Nq)
 
     def decode(self, a: np.ndarray, dtype: str) -> np.ndarray:

@@ -8,7 +8,8 @@
  *
  * What it computes (the textbook definition, not the tiled algorithm):
  *   For each batch b, head h and query row i,
- *     J(i)   = { j : 0 <= j < L_b and (not causal or j <= i) }     (masked keys excluded)
+ *     J(i)   = { j : 0 <= j < L_b and (not causal or j <= i)
+ *                    and (w < 0 or i - w <= j <= i + w) }          (masked keys excluded)
  *     s_j    = scale * sum_d q[i,d] k[j,d]                          for j in J(i)
  *     m      = max_j s_j                                            (two-pass max shift)
  *     e_j    = exp(s_j - m),  l = sum_j e_j
@@ -24,6 +25,10 @@
  *     fill conventions on every row that keeps at least one key.
  *   - causal mask = attend only to the current and earlier positions: hotelren.com
  *     sec.2.1 note 2; lshu.cn sec.3.1.  Read here as j <= i (top-left aligned).
+ *   - local (sliding-window) attention: each position attends only to the w positions before
+ *     and after it, every other weight is zero: lshu.cn sec.2 ("localization", Longformer /
+ *     BigBird windows); aicoding.csdn.net sec.4.3 (window w = 512).  Read here as the band
+ *     |i - j| <= w, combined with the causal and padding masks; w < 0 means no window.
  *   - max-shifted softmax and log-sum-exp = max + log(sum exp(x - max)):
  *     aicoding.csdn.net sec.2.2 ("numerical stability of softmax", chunked logsumexp).
  *   - the fused method is numerically the same as the plain one: aicoding.csdn.net ch.1
@@ -81,8 +86,8 @@ static void decode_row(const void* base, int dtype, int64_t off, int D, double* 
 
 /* One query row (b, h, i).  Scratch: qrow[D], s[Nk]. */
 static void one_row(const void* q, const void* k, const void* v, int dtype, int H, int Nq,
-                    int Nk, int D, double scale, int causal, const int32_t* key_lens, int64_t row,
-                    double* o, double* lse, double* qrow, double* s, double* krow) {
+                    int Nk, int D, double scale, int causal, int window, const int32_t* key_lens,
+                    int64_t row, double* o, double* lse, double* qrow, double* s, double* krow) {
     int64_t bh = row / Nq;
     int i = (int)(row % Nq);
     int b = (int)(bh / H);
@@ -92,10 +97,14 @@ static void one_row(const void* q, const void* k, const void* v, int dtype, int 
         if (L < 0) L = 0;
         if (L > Nk) L = Nk;
     }
-    int64_t jend = L; /* J(i) = [0, jend) */
+    int64_t jbeg = 0, jend = L; /* J(i) = [jbeg, jend) */
     if (causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;
+    if (window >= 0) {
+        if (jbeg < (int64_t)i - window) jbeg = (int64_t)i - window;
+        if (jend > (int64_t)i + window + 1) jend = (int64_t)i + window + 1;
+    }
 
-    if (jend <= 0) {
+    if (jend <= jbeg) {
         for (int d = 0; d < D; ++d) o[d] = 0.0;
         *lse = -INFINITY;
         return;
@@ -103,27 +112,28 @@ static void one_row(const void* q, const void* k, const void* v, int dtype, int 
     decode_row(q, dtype, row * D, D, qrow);
     int64_t kbase = bh * (int64_t)Nk * D;
 
-    /* logits */
-    for (int64_t j = 0; j < jend; ++j) {
+    /* logits; s[j - jbeg] holds key j */
+    for (int64_t j = jbeg; j < jend; ++j) {
         decode_row(k, dtype, kbase + j * D, D, krow);
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc += qrow[d] * krow[d];
-        s[j] = scale * acc;
+        s[j - jbeg] = scale * acc;
     }
+    const int64_t n = jend - jbeg;
     /* pass 1: max */
     double m = s[0];
-    for (int64_t j = 1; j < jend; ++j)
+    for (int64_t j = 1; j < n; ++j)
         if (s[j] > m) m = s[j];
     /* pass 2: shifted exponentials and their sum */
     double l = 0.0;
-    for (int64_t j = 0; j < jend; ++j) {
+    for (int64_t j = 0; j < n; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
     }
     /* weighted sum of values */
     for (int d = 0; d < D; ++d) o[d] = 0.0;
-    for (int64_t j = 0; j < jend; ++j) {
-        decode_row(v, dtype, kbase + j * D, D, krow);
+    for (int64_t j = 0; j < n; ++j) {
+        decode_row(v, dtype, kbase + (jbeg + j) * D, D, krow);
         for (int d = 0; d < D; ++d) o[d] += s[j] * krow[d];
     }
     for (int d = 0; d < D; ++d) o[d] /= l;
@@ -131,17 +141,19 @@ static void one_row(const void* q, const void* k, const void* v, int dtype, int 
 }
 
 /*
- * oracle_attn_rows -- reference attention on selected query rows.
+ * oracle_attn_rows_window -- reference attention on selected query rows.
  *   q: [B,H,Nq,D], k, v: [B,H,Nk,D], contiguous, stored as `dtype` (0 fp32, 1 fp16, 2 bf16).
+ *   window: half-width w of the local band |i - j| <= w, or any negative value for none.
  *   key_lens: int32[B] or NULL (every key valid); values are clamped to [0, Nk].
  *   rows: flat row ids ((b*H + h)*Nq + i), or NULL for all B*H*Nq rows in order.
  *   o: fp64 [nrows, D]; lse: fp64 [nrows].
  *   nthreads <= 0 uses the OpenMP default.
  * Returns 0, -1 on a bad argument, -2 if scratch memory cannot be allocated.
  */
-int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int B, int H, int Nq,
-                     int Nk, int D, double scale, int causal, const int32_t* key_lens,
-                     const int64_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
+int oracle_attn_rows_window(const void* q, const void* k, const void* v, int dtype, int B, int H,
+                            int Nq, int Nk, int D, double scale, int causal, int window,
+                            const int32_t* key_lens, const int64_t* rows, int64_t nrows, double* o,
+                            double* lse, int nthreads) {
     if (!q || !k || !v || !o || !lse) return -1;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
     if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return -1;
@@ -170,12 +182,20 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int
 #pragma omp for schedule(dynamic, 16)
         for (int64_t r = 0; r < nrows; ++r) {
             int64_t row = rows ? rows[r] : r;
-            one_row(q, k, v, dtype, H, Nq, Nk, D, scale, causal, key_lens, row, o + r * D, lse + r,
-                    qrow, s, krow);
+            one_row(q, k, v, dtype, H, Nq, Nk, D, scale, causal, window, key_lens, row, o + r * D,
+                    lse + r, qrow, s, krow);
         }
     }
     free(scratch);
     return 0;
+}
+
+/* oracle_attn_rows -- the same without a window. */
+int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int B, int H, int Nq,
+                     int Nk, int D, double scale, int causal, const int32_t* key_lens,
+                     const int64_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
+    return oracle_attn_rows_window(q, k, v, dtype, B, H, Nq, Nk, D, scale, causal, -1, key_lens,
+                                   rows, nrows, o, lse, nthreads);
 }
 
 /* Decoders exposed for the tests' checks of the widening itself. */

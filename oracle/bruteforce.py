@@ -4,7 +4,8 @@ Pure-Python `decimal` arithmetic at 50 significant digits (Decimal.exp and Decim
 correctly rounded), so for inputs that are exact binary fractions the result is the exact
 attention output to ~1e-48.  It follows the same plain definition as attn_oracle.c but
 shares no code with it: masked keys are left out of the softmax, the causal mask keeps
-keys j <= i, and a row with no key gives O = 0 and LSE = -inf.
+keys j <= i, a window w keeps keys with |i - j| <= w, and a row with no key gives O = 0 and
+LSE = -inf.
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def attention_row(q_row, keys, values, scale, digits: int = 50):
         return out, m + tot.ln()
 
 
-def attention(q, k, v, scale, causal=False, key_lens=None, digits: int = 50):
+def attention(q, k, v, scale, causal=False, key_lens=None, digits: int = 50, window=None):
     """q: nested lists [B][H][Nq][D]; k, v: [B][H][Nk][D].  Returns (O, LSE) as nested lists of
     Decimal (LSE None for empty rows)."""
     B, H = len(q), len(q[0])
@@ -59,8 +60,10 @@ def attention(q, k, v, scale, causal=False, key_lens=None, digits: int = 50):
             kb = Nk if key_lens is None else max(0, min(Nk, int(key_lens[b])))
             oh, lh = [], []
             for i, qr in enumerate(q[b][h]):
-                jend = min(kb, i + 1) if causal else kb
-                o, lse = attention_row(qr, k[b][h][:jend], v[b][h][:jend], scale, digits)
+                keep = [j for j in range(kb)
+                        if (not causal or j <= i) and (window is None or abs(i - j) <= window)]
+                o, lse = attention_row(qr, [k[b][h][j] for j in keep], [v[b][h][j] for j in keep],
+                                       scale, digits)
                 oh.append(o)
                 lh.append(lse)
             ob.append(oh)

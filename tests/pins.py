@@ -7,7 +7,9 @@ of the oracle source in test_oracle_mutants.py, which shows that each plausible 
 is caught by at least one of them.
 
 What the pins rest on (none of them re-types the oracle's formula):
-  * closed forms: Q = 0 or scale = 0 gives the mean of the valid V rows and LSE = ln|J|;
+  * closed forms: Q = 0 or scale = 0 gives the mean of the valid V rows and LSE = ln|J|
+    (with a local window too); a window of 0 copies V[i]; a window wider than the sequence
+    changes nothing;
     causal row 0 copies V[0]; one key copies it; two keys give a logistic mix; a dominant
     key with a logit gap g gives a known weighted mix (and an overflow trap when g is huge);
   * invariants: rows of the attention matrix sum to one (V = 1 gives O = 1; V = identity
@@ -291,7 +293,7 @@ def pin_chunked_lse(impl):
 
 
 # ---------------------------------------------------------------- library special case
-def torch_sdpa_f64(q, k, v, dtype, scale, causal, key_lens):
+def torch_sdpa_f64(q, k, v, dtype, scale, causal, key_lens, window=None):
     """torch's scaled_dot_product_attention in float64 on the CPU, with a boolean mask where
     True = may attend (the convention the pages state).  Rows with no valid key are NaN."""
     import torch
@@ -300,6 +302,10 @@ def torch_sdpa_f64(q, k, v, dtype, scale, causal, key_lens):
     B, H, Nq, _ = qd.shape
     Nk = kd.shape[2]
     allow = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+    if window is not None:
+        i = torch.arange(Nq)[:, None]
+        j = torch.arange(Nk)[None, :]
+        allow &= ((i - j).abs() <= window)[None, None]
     if key_lens is not None:
         j = torch.arange(Nk)
         allow &= (j[None, :] < torch.from_numpy(np.asarray(key_lens, np.int64))[:, None])[:, None, None, :]
@@ -331,6 +337,80 @@ def pin_torch_sdpa_small(impl):
                 close(lse, rl, 1e-13, f"sdpa lse {dtype} causal={causal} padded={padded}")
 
 
+def pin_torch_sdpa_window(impl):
+    """Local windows against torch with a band mask (True = may attend), rows that keep no key
+    excluded (torch gives NaN there, the definition here gives O = 0 and LSE = -inf)."""
+    rng = np.random.default_rng(22)
+    for dtype in ("f32", "bf16"):
+        for causal in (False, True):
+            for window in (0, 1, 3, 7):
+                B, H, Nq, Nk, D = 2, 2, 12, 10, 8
+                q = rand_store(rng, (B, H, Nq, D), dtype)
+                k = rand_store(rng, (B, H, Nk, D), dtype)
+                v = rand_store(rng, (B, H, Nk, D), dtype)
+                kl = np.array([10, 5], np.int32)
+                scale = float(np.float32(1 / math.sqrt(D)))
+                o, lse = impl.attn(q, k, v, dtype, scale, causal, kl, window=window)
+                ro, rl = torch_sdpa_f64(q, k, v, dtype, scale, causal, kl, window)
+                live = np.isfinite(rl)
+                assert np.all(lse[~live] == -np.inf) and np.all(o[~live] == 0.0), "empty window rows"
+                close(o[live], ro[live], 1e-13, f"sdpa window={window} O {dtype} causal={causal}")
+                close(lse[live], rl[live], 1e-13, f"sdpa window={window} lse {dtype} causal={causal}")
+
+
+def window_set(i, L, causal, w):
+    """The keys row i may attend to, written out from the band's definition |i - j| <= w."""
+    return [j for j in range(L) if (not causal or j <= i) and abs(i - j) <= w]
+
+
+def pin_window_zero_query_mean(impl):
+    """Q = 0 with a window: O is the mean of V over the band's valid keys, LSE = ln of their count."""
+    rng = np.random.default_rng(23)
+    for causal in (False, True):
+        for w in (0, 2, 5):
+            B, H, Nq, Nk, D = 2, 1, 9, 8, 4
+            q = store(np.zeros((B, H, Nq, D)), "f32")
+            k = rand_store(rng, (B, H, Nk, D), "f32")
+            v = rand_store(rng, (B, H, Nk, D), "f32")
+            kl = np.array([8, 4], np.int32)
+            o, lse = impl.attn(q, k, v, "f32", 0.7, causal, kl, window=w)
+            vd = v.astype(np.float64)
+            for b in range(B):
+                for i in range(Nq):
+                    keep = window_set(i, int(kl[b]), causal, w)
+                    if not keep:
+                        assert np.all(o[b, 0, i] == 0.0) and lse[b, 0, i] == -np.inf, "empty band"
+                        continue
+                    close(o[b, 0, i], vd[b, 0, keep].mean(axis=0), 1e-14, f"window {w} Q=0 mean")
+                    close(lse[b, 0, i], math.log(len(keep)), 1e-14, f"window {w} Q=0 lse")
+
+
+def pin_window_extremes(impl):
+    """A window of 0 copies V[i] (LSE = the diagonal logit); a window at least as wide as the
+    sequence is the same computation as no window at all (bit for bit)."""
+    rng = np.random.default_rng(24)
+    for dtype in ("f32", "bf16"):
+        B, H, Nq, Nk, D = 2, 2, 7, 6, 8
+        q, k, v = (rand_store(rng, (B, H, n, D), dtype) for n in (Nq, Nk, Nk))
+        kl = np.array([6, 3], np.int32)
+        for causal in (False, True):
+            o, lse = impl.attn(q, k, v, dtype, 0.5, causal, kl, window=0)
+            qd, kd, vd = (storage_to_f64(t, dtype) for t in (q, k, v))
+            for b in range(B):
+                for i in range(Nq):
+                    if i >= kl[b]:
+                        assert np.all(o[b, :, i] == 0.0) and np.all(lse[b, :, i] == -np.inf)
+                        continue
+                    assert np.array_equal(o[b, :, i], vd[b, :, i]), "window 0 must copy V[i]"
+                    for h in range(H):
+                        exact = Fraction(0.5) * sum(Fraction(a) * Fraction(c)
+                                                    for a, c in zip(qd[b, h, i], kd[b, h, i]))
+                        close(lse[b, h, i], float(exact), 1e-13, "window 0 lse")
+            o1, l1 = impl.attn(q, k, v, dtype, 0.5, causal, kl, window=max(Nq, Nk))
+            o2, l2 = impl.attn(q, k, v, dtype, 0.5, causal, kl)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "wide window must equal no window"
+
+
 # ---------------------------------------------------------------- brute force
 def _golden_cases():
     with open(os.path.join(HERE, "golden", "bruteforce_tiny.json")) as f:
@@ -343,7 +423,7 @@ def pin_golden_bruteforce(impl):
         for dtype in ("f32", "bf16", "f16"):
             q, k, v = (store(np.array(cs[n]), dtype) for n in "qkv")
             kl = None if cs["key_lens"] is None else np.array(cs["key_lens"], np.int32)
-            o, lse = impl.attn(q, k, v, dtype, cs["scale"], cs["causal"], kl)
+            o, lse = impl.attn(q, k, v, dtype, cs["scale"], cs["causal"], kl, window=cs.get("window"))
             want_o = np.array(cs["o"], dtype=np.float64)
             want_l = np.array([[[float(x) for x in h] for h in b] for b in cs["lse"]])
             close(o, want_o, 2e-15, f"golden {cs['name']} O")
@@ -371,5 +451,6 @@ ALL_PINS = [
     pin_zero_query_mean, pin_scale_zero, pin_causal_row0, pin_single_key, pin_two_keys,
     pin_one_hot_dominant, pin_huge_logit_gap, pin_empty_rows, pin_rows_sum_to_one,
     pin_permutations, pin_key_shift, pin_chunked_lse, pin_torch_sdpa_small,
+    pin_torch_sdpa_window, pin_window_zero_query_mean, pin_window_extremes,
     pin_golden_bruteforce, pin_decoders,
 ]

@@ -9,8 +9,8 @@ import oracle
 import pins
 
 MUTANTS = [
-    ("dropped scale", "s[j] = scale * acc;", "s[j] = acc;"),
-    ("scale applied twice", "s[j] = scale * acc;", "s[j] = scale * scale * acc;"),
+    ("dropped scale", "s[j - jbeg] = scale * acc;", "s[j - jbeg] = acc;"),
+    ("scale applied twice", "s[j - jbeg] = scale * acc;", "s[j - jbeg] = scale * scale * acc;"),
     ("q.q instead of q.k", "acc += qrow[d] * krow[d];", "acc += qrow[d] * qrow[d];"),
     ("wrong sign in the shift", "s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
     ("no max shift", "if (s[j] > m) m = s[j];", "if (s[j] > m) m = m;"),
@@ -24,10 +24,17 @@ MUTANTS = [
     ("key length off by one", "L = key_lens[b];", "L = key_lens[b] - 1;"),
     ("batch index from head", "int b = (int)(bh / H);", "int b = (int)(bh % H);"),
     ("K/V base uses Nq", "int64_t kbase = bh * (int64_t)Nk * D;", "int64_t kbase = bh * (int64_t)Nq * D;"),
-    ("V rows reversed", "decode_row(v, dtype, kbase + j * D, D, krow);",
+    ("V rows reversed", "decode_row(v, dtype, kbase + (jbeg + j) * D, D, krow);",
      "decode_row(v, dtype, kbase + (jend - 1 - j) * D, D, krow);"),
-    ("V read from K", "decode_row(v, dtype, kbase + j * D, D, krow);",
-     "decode_row(k, dtype, kbase + j * D, D, krow);"),
+    ("V read from K", "decode_row(v, dtype, kbase + (jbeg + j) * D, D, krow);",
+     "decode_row(k, dtype, kbase + (jbeg + j) * D, D, krow);"),
+    ("V rows not offset by the window start", "decode_row(v, dtype, kbase + (jbeg + j) * D, D, krow);",
+     "decode_row(v, dtype, kbase + j * D, D, krow);"),
+    ("logits not offset by the window start", "s[j - jbeg] = scale * acc;", "s[j] = scale * acc;"),
+    ("window start off by one", "jbeg = (int64_t)i - window;", "jbeg = (int64_t)i - window + 1;"),
+    ("window start ignored", "if (jbeg < (int64_t)i - window) jbeg = (int64_t)i - window;", ""),
+    ("window end off by one", "jend = (int64_t)i + window + 1;", "jend = (int64_t)i + window;"),
+    ("window end ignored", "if (jend > (int64_t)i + window + 1) jend = (int64_t)i + window + 1;", ""),
     ("empty row LSE 0", "*lse = -INFINITY;", "*lse = 0.0;"),
     ("bf16 shift 15", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
     ("fp16 bias off by one", "e - 25);", "e - 24);"),
