@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·D, causal halved) and % of bf16 MFMA peak"
+METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4·D per (query, key) pair inside the band)"
 # MI355X published dense peaks (256 CUs at 2.4 GHz).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
@@ -71,7 +72,11 @@ def row_pairs(w, rows, key_lens):
     b = rows // (w.H * w.Nq)
     L = np.full(rows.shape, w.Nk, dtype=np.int64) if key_lens is None else \
         np.clip(key_lens.astype(np.int64), 0, w.Nk)[b]
-    return np.minimum(L, i + 1) if w.causal else L
+    hi = np.minimum(L, i + 1) if w.causal else L
+    if w.window is None:
+        return hi
+    hi = np.minimum(hi, i + w.window + 1)
+    return np.maximum(hi - np.maximum(i - w.window, 0), 0)
 
 
 def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
@@ -93,7 +98,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
         n = min(n, total)
         rows = np.sort(rng.choice(total, size=n, replace=False)) if n < total else np.arange(total)
         t0 = time.perf_counter()
-        ro, rl = impl.attn_rows(*args, rows=rows)
+        ro, rl = impl.attn_rows(*args, rows=rows, window=w.window)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or n >= total:
             break
@@ -170,7 +175,8 @@ def main():
     scale = float(x["scale"])
 
     def step():
-        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream)
+        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream,
+                    window=w.window)
 
     for _ in range(a.warmup):
         step()
@@ -218,7 +224,7 @@ def main():
     abytes = algorithmic_bytes(w)
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if w.window is None else METRIC_WINDOW,
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -231,7 +237,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
-                   "causal": w.causal, "key_padding": w.padded, "seed": x["seed"],
+                   "causal": w.causal, "key_padding": w.padded, "window": w.window, "seed": x["seed"],
                    "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

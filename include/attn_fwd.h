@@ -48,7 +48,8 @@ typedef enum {
     ATTN_ERR_SCALE = -5,    /* scale is not finite */
     ATTN_ERR_FLAG = -6,     /* causal is not 0 or 1 */
     ATTN_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
-    ATTN_ERR_ALIGN = -8     /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
+    ATTN_ERR_ALIGN = -8,    /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
+    ATTN_ERR_WINDOW = -9    /* window is below -1 (attn_fwd_window) */
 } attn_status;
 
 /*
@@ -82,6 +83,25 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
              void* stream);
+
+/*
+ * attn_fwd_window -- attn_fwd restricted to a local band (sliding-window attention): row i
+ * attends only to keys j with |i - j| <= window, on top of the causal and padding rules above.
+ * Source: the local-window method in which each position attends to the positions within a
+ * window before and after it and every other weight is zero (lshu.cn page, sec.2,
+ * "localization", Longformer / BigBird windows; aicoding.csdn.net page, sec.4.3, w = 512).
+ * With causal = 1 the band keeps i - window <= j <= i.
+ *
+ *   window   -1 for no band (then identical to attn_fwd), or >= 0.  A band at least as wide as
+ *            max(Nq, Nk) is no band.  Key tiles outside every row's band are never read, so
+ *            the work falls with the band.
+ *   other arguments, layout, ownership and errors as attn_fwd; window < -1 returns
+ *   ATTN_ERR_WINDOW and writes nothing.  A row whose band holds no valid key gets O = 0 and
+ *   LSE = -inf.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int Nq, int Nk, int D, float scale, int causal, int window,
+                    const int32_t* key_lens, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

@@ -30,11 +30,11 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 
 
-def run(x: dict, dtype: str, causal: bool, scale=None, dev="cuda"):
+def run(x: dict, dtype: str, causal: bool, scale=None, dev="cuda", window=None):
     q, k, v = (to_device(x[n], dtype, dev) for n in "qkv")
     kl = None if x.get("key_lens") is None else torch.from_numpy(np.asarray(x["key_lens"], np.int32)).to(dev)
     s = float(x["scale"]) if scale is None else float(scale)
-    o, lse = binding.fwd(q, k, v, causal=causal, key_lens=kl, scale=s)
+    o, lse = binding.fwd(q, k, v, causal=causal, key_lens=kl, scale=s, window=window)
     torch.cuda.synchronize()
     return o, lse
 

@@ -66,6 +66,21 @@ def test_host_validation(over, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(window=-2), -9), (dict(window=-(1 << 30)), -9), (dict(q=None), -1), (dict(D=32), -3),
+    (dict(causal=2), -6), (dict(o=FAKE + 8), -8), (dict(window=-2, causal=3), -6),
+])
+def test_host_validation_window(over, code):
+    """attn_fwd_window checks its band argument on the host like the others."""
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=8, Nk=8, D=64, scale=0.125,
+             causal=0, window=3, key_lens=None, dtype=2, stream=None)
+    a.update(over)
+    rc = binding.attn_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                 a["Nk"], a["D"], a["scale"], a["causal"], a["window"],
+                                 a["key_lens"], a["dtype"], a["stream"])
+    assert rc == code
+
+
 def test_missing_library_fails_loudly():
     code = ("import sys; sys.path.insert(0, %r)\n"
             "from transformer_scaled_dot_amd import binding\n"

@@ -95,9 +95,9 @@ def test_edge_cases(case, dtype, oracle_impl):
 
 
 # ------------------------------------------------------------------ closed forms on the kernel
-def _kernel(q, k, v, dtype, scale, causal=False, key_lens=None):
+def _kernel(q, k, v, dtype, scale, causal=False, key_lens=None, window=None):
     x = {"q": q, "k": k, "v": v, "scale": np.float32(scale), "key_lens": key_lens}
-    return run(x, dtype, causal)
+    return run(x, dtype, causal, window=window)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -217,7 +217,7 @@ def test_kernel_golden_bruteforce():
             pad = lambda a: np.pad(np.array(a, np.float64), [(0, 0)] * 3 + [(0, 64 - D)])
             q, k, v = (pins.store(pad(cs[n]), dtype) for n in "qkv")
             kl = None if cs["key_lens"] is None else np.array(cs["key_lens"], np.int32)
-            o, lse = _kernel(q, k, v, dtype, cs["scale"], cs["causal"], kl)
+            o, lse = _kernel(q, k, v, dtype, cs["scale"], cs["causal"], kl, cs.get("window"))
             o, lse = to_f64(o), to_f64(lse)
             assert np.all(o[..., D:] == 0)
             want_o = np.array(cs["o"], np.float64)

@@ -88,3 +88,15 @@ def test_stress_variant_scales_q_and_k_only():
 def test_flop_formula():
     w = inputs.WORKLOADS["longctx_causal_bf16_b1h32n16384d128"]
     assert w.flops() == 4 * 32 * 16384 * 16384 * 128 / 2
+
+
+def test_band_pair_count():
+    """The windowed FLOP count is 4*B*H*D times the pairs with |i - j| <= w (and j <= i when
+    causal), counted here by brute force on small shapes."""
+    for causal in (False, True):
+        for w in (0, 1, 5, 40):
+            wl = inputs.Workload("t", "bf16", 2, 3, 37, 29, 64, causal, False, 1.0, 1.0, 1, window=w)
+            brute = sum(1 for i in range(37) for j in range(29)
+                        if abs(i - j) <= w and (not causal or j <= i))
+            assert wl.band_pairs() == brute
+            assert wl.flops() == 4.0 * 2 * 3 * 64 * brute

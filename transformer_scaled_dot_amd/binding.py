@@ -1,8 +1,9 @@
 """Python binding of the C ABI in include/attn_fwd.h (argument marshalling only).
 
-`attn_fwd` and `attn_status_str` mirror the C entry points one to one (raw device pointers,
-sizes, a stream handle).  `fwd` is the tensor-level convenience: it checks the tensors on the
-host, allocates O and LSE with torch on the current stream and calls `attn_fwd`.  Every step of
+`attn_fwd`, `attn_fwd_window` and `attn_status_str` mirror the C entry points one to one (raw
+device pointers, sizes, a stream handle).  `fwd` is the tensor-level convenience: it checks the
+tensors on the host, allocates O and LSE with torch on the current stream and calls
+`attn_fwd` (or `attn_fwd_window` when a local window is asked for).  Every step of
 the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
 module raises instead of computing anything itself.
 """
@@ -20,9 +21,9 @@ ATTN_OK = 0
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_FLAG", -7: "ATTN_ERR_LAUNCH",
-    -8: "ATTN_ERR_ALIGN",
+    -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW",
 }
-EXPORTS = ("attn_fwd", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_status_str")
 
 _lib = None
 
@@ -48,6 +49,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
     ]
+    lib.attn_fwd_window.restype = ctypes.c_int
+    lib.attn_fwd_window.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+    ]
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -58,6 +65,13 @@ def attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, s
     """The C entry point: device pointers as ints (or None), sizes, dtype code, stream handle."""
     return load_library().attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens,
                                    dtype, stream)
+
+
+def attn_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, key_lens, dtype,
+                    stream) -> int:
+    """The C entry point with a local band |i - j| <= window (-1: no band)."""
+    return load_library().attn_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window,
+                                          key_lens, dtype, stream)
 
 
 def attn_status_str(status: int) -> str:
@@ -79,9 +93,10 @@ def dtype_code(t) -> int:
 
 
 def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None, out=None,
-        lse=None, stream=None):
+        lse=None, stream=None, window: int | None = None):
     """O, LSE = attention(q, k, v).  q: [B,H,Nq,D]; k, v: [B,H,Nk,D]; all contiguous CUDA tensors
     of one dtype; key_lens: int32 [B] on the same device or None.  scale defaults to 1/sqrt(D).
+    window=w keeps only keys with |i - j| <= w (sliding-window attention); None: every key.
     Returns O (q's dtype, [B,H,Nq,D]) and LSE (float32, [B,H,Nq])."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -108,6 +123,8 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
         scale = 1.0 / math.sqrt(D)
     if not math.isfinite(scale):
         raise ValueError("scale must be finite")
+    if window is not None and (int(window) != window or window < 0):
+        raise ValueError("window must be None or an integer >= 0")
     kl_ptr = None
     if key_lens is not None:
         if (not isinstance(key_lens, torch.Tensor) or key_lens.dtype != torch.int32
@@ -127,8 +144,13 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                  B, H, Nq, Nk, D, float(scale), int(bool(causal)), kl_ptr, code, handle)
+    if window is None:
+        rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, Nq, Nk, D, float(scale), int(bool(causal)), kl_ptr, code, handle)
+    else:
+        rc = attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                             min(int(window), 2**31 - 1), kl_ptr, code, handle)
     if rc != ATTN_OK:
         raise AttnError(rc)
     return out, lse

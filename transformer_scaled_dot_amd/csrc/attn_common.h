@@ -20,7 +20,20 @@ struct Params {
     float scale_log2;  // max(|scale| * log2(e), 1e-30): logits are handled in base-2 units
     int negate_q;      // scale < 0: the sign is moved onto Q (an exact bit flip)
     int causal;
+    int window;        // half-width w of the local band |i - j| <= w, or -1 for none
 };
+
+// Keys [lo, hi) that row i may attend to, before the padding length: the causal rule keeps
+// j <= i, the local band keeps |i - j| <= w.
+__device__ __forceinline__ int row_key_lo(const Params& p, int i) {
+    return p.window >= 0 ? i - p.window : 0;
+}
+__device__ __forceinline__ int row_key_hi(const Params& p, int i, int kv_valid) {
+    int hi = kv_valid;
+    if (p.causal) hi = min(hi, i + 1);
+    if (p.window >= 0) hi = min(hi, i + p.window + 1);
+    return hi;
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).
 // Renumber them so that each XCD walks one contiguous range of the logical order: the

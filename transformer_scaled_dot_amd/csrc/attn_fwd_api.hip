@@ -5,15 +5,16 @@
 #include <attn_fwd.h>
 #include "attn_common.h"
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int H, int Nq, int Nk, int D, float scale, int causal,
-                        const int32_t* key_lens, int dtype, void* stream) {
+extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                               int window, const int32_t* key_lens, int dtype, void* stream) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+    if (window < -1) return ATTN_ERR_WINDOW;
     if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) != 0 ||
         ((uintptr_t)key_lens & 3) != 0)
         return ATTN_ERR_ALIGN;
@@ -46,10 +47,19 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     p.scale_log2 = (float)fmax(fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.f;
     p.causal = causal;
+    // |i - j| < max(Nq, Nk) always holds: a band at least that wide is no band.
+    p.window = window >= (Nq > Nk ? Nq : Nk) ? -1 : window;
 
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = dtype == ATTN_F32 ? attn_launch_f32(p, D, s) : attn_launch_mfma(p, dtype, D, s);
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Nq, int Nk, int D, float scale, int causal,
+                        const int32_t* key_lens, int dtype, void* stream) {
+    return attn_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, -1, key_lens, dtype,
+                           stream);
 }
 
 extern "C" const char* attn_status_str(int status) {
@@ -63,6 +73,7 @@ extern "C" const char* attn_status_str(int status) {
         case ATTN_ERR_FLAG: return "causal must be 0 or 1";
         case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned, key_lens 4-byte aligned";
+        case ATTN_ERR_WINDOW: return "window must be -1 (no band) or >= 0";
         default: return "unknown status";
     }
 }

@@ -38,9 +38,12 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
     }
 
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
+    const int q_last = min(p.Nq, q0 + BMF) - 1;
     int kv_end = kv_valid;
-    if (p.causal) kv_end = min(kv_end, min(p.Nq, q0 + BMF));
-    const int lim = p.causal ? min(kv_valid, qi + 1) : kv_valid;
+    if (p.causal) kv_end = min(kv_end, q_last + 1);
+    if (p.window >= 0) kv_end = min(kv_end, q_last + p.window + 1);
+    const int kv_begin = p.window >= 0 ? max(0, q0 - p.window) / BNF * BNF : 0;
+    const int lo = attn::row_key_lo(p, qi), hi = attn::row_key_hi(p, qi, kv_valid);
     const float c2 = p.scale_log2;
 
     float o[D];
@@ -48,7 +51,7 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
     for (int d = 0; d < D; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int j0 = 0; j0 < kv_end; j0 += BNF) {
+    for (int j0 = kv_begin; j0 < kv_end; j0 += BNF) {
         __syncthreads();
         for (int idx = tid; idx < BNF * D; idx += BMF) {
             const int row = idx / D, d = idx % D;
@@ -65,7 +68,7 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
             float acc = 0.f;
 #pragma unroll 16
             for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qs[tid][d], ks[jj][d], acc);
-            const float t = (j0 + jj < lim) ? acc * c2 : -INFINITY;
+            const float t = (j0 + jj >= lo && j0 + jj < hi) ? acc * c2 : -INFINITY;
             s[jj] = t;
             mt = fmaxf(mt, t);
         }

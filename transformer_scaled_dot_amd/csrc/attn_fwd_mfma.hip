@@ -22,8 +22,9 @@
 //     reference max is raised (and O, l rescaled) only when a row's tile max exceeds it by more
 //     than 2^8; otherwise P is formed against the stale reference, which leaves O / l and
 //     ln 2 (m + log2 l) unchanged;
-//   * tiles beyond a row's last valid key are never loaded (causal and key padding); masks
-//     are evaluated only on the tiles that straddle a boundary.
+//   * tiles outside every row's visible keys are never loaded (causal, key padding and the
+//     local band |i - j| <= w of sliding-window attention, lshu.cn page sec.2); masks are
+//     evaluated only on the tiles that straddle a boundary.
 #include "attn_common.h"
 
 namespace {
@@ -118,10 +119,14 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int qw0 = q0 + wave * 32;
     const int qi = qw0 + r;
 
+    // Key tiles [t_begin, n_tiles) hold every key some row of this workgroup may see.
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
+    const int q_last = min(p.Nq, q0 + BM) - 1;
     int kv_end = kv_valid;
-    if (p.causal) kv_end = min(kv_end, min(p.Nq, q0 + BM));
+    if (p.causal) kv_end = min(kv_end, q_last + 1);
+    if (p.window >= 0) kv_end = min(kv_end, q_last + p.window + 1);
     const int n_tiles = (kv_end + BN - 1) / BN;
+    const int t_begin = p.window >= 0 ? max(0, q0 - p.window) / BN : 0;
 
     const T* qg = (const T*)p.q + (size_t)bh * p.Nq * D;
     const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
@@ -206,7 +211,10 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
 
         const int j0 = it * BN;
-        if (!wave_has_rows || (p.causal && j0 > qw0 + 31)) return;  // nothing visible here
+        // nothing visible to this wave's rows qw0 .. qw0+31 in keys j0 .. j0+BN-1
+        if (!wave_has_rows || j0 >= attn::row_key_hi(p, qw0 + 31, kv_valid) ||
+            j0 + BN <= attn::row_key_lo(p, qw0))
+            return;
         const lds_u8* kb = smem + stage * STAGE;
         const lds_u8* vb = kb + TILE;
 
@@ -223,17 +231,19 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         }
 
         // ---- online softmax.  Register i of s[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.
-        const bool need_mask = (j0 + BN > kv_valid) || (p.causal && j0 + BN - 1 > qw0);
+        // a mask applies unless every key of the tile is visible to every row of the wave
+        const bool need_mask = j0 + BN > attn::row_key_hi(p, qw0, kv_valid) ||
+                               j0 < attn::row_key_lo(p, qw0 + 31);
         float mt;
         if (need_mask) {
-            const int lim = p.causal ? min(kv_valid, qi + 1) : kv_valid;
+            const int lo = attn::row_key_lo(p, qi), hi = attn::row_key_hi(p, qi, kv_valid);
             mt = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const float t = j < lim ? s[kt][i] * c2 : -INFINITY;
+                    const float t = (j >= lo && j < hi) ? s[kt][i] * c2 : -INFINITY;
                     s[kt][i] = t;
                     mt = fmaxf(mt, t);
                 }
@@ -302,8 +312,8 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         }
     };
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int it = 0; it < n_tiles; it += 2) {
+    if (t_begin < n_tiles) issue_tile(t_begin, 0);
+    for (int it = t_begin; it < n_tiles; it += 2) {
         do_tile(it, 0);
         if (it + 1 < n_tiles) do_tile(it + 1, 1);
     }

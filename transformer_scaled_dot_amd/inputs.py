@@ -120,14 +120,26 @@ class Workload:
     seed: int
     note: str = ""
     scale: float = field(default=None)  # defaults to 1/sqrt(D), rounded to float32
+    window: int = field(default=None)   # local band |i - j| <= window, None for none
 
     @property
     def scale_f32(self) -> np.float32:
         s = self.scale if self.scale is not None else 1.0 / np.sqrt(self.D)
         return np.float32(s)
 
+    def band_pairs(self) -> int:
+        """(query, key) pairs inside the band (and the causal triangle), padding ignored."""
+        i = np.arange(self.Nq, dtype=np.int64)
+        lo = np.maximum(i - self.window, 0)
+        hi = np.minimum(i + 1 if self.causal else i + self.window + 1, self.Nk)
+        hi = np.minimum(hi, i + self.window + 1)
+        return int(np.maximum(hi - lo, 0).sum())
+
     def flops(self) -> float:
-        """Metric FLOPs: 4*B*H*Nq*Nk*D, halved for causal (QK^T and PV, dense count)."""
+        """Metric FLOPs: 4*B*H*Nq*Nk*D, halved for causal (QK^T and PV, dense count).  With a
+        local window: 4*B*H*D per (query, key) pair inside the band."""
+        if self.window is not None:
+            return 4.0 * self.B * self.H * self.D * self.band_pairs()
         f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.D
         return f / 2 if self.causal else f
 
@@ -150,10 +162,15 @@ WORKLOADS = {
                  "decoder causal attention at 4K"),
         Workload("longctx_causal_bf16_b1h32n16384d128", "bf16", 1, 32, 16384, 16384, 128, True, False, 0.5, 0.5, 5,
                  "long-context causal attention at 16K"),
+        Workload("decoder_window512_causal_bf16_b4h32n4096d128", "bf16", 4, 32, 4096, 4096, 128, True, False,
+                 0.5, 0.5, 6, "decoder causal attention at 4K with a sliding window of 512", window=512),
+        Workload("longctx_window512_causal_bf16_b1h32n16384d128", "bf16", 1, 32, 16384, 16384, 128, True,
+                 False, 0.5, 0.5, 7, "long-context causal attention at 16K with a sliding window of 512",
+                 window=512),
     ]
 }
 
-# The measured workload of the benchmark and the five parity workloads, in order.
+# The measured workload of the benchmark and the parity workloads, in order.
 BENCH_WORKLOAD = "longctx_causal_bf16_b1h32n16384d128"
 PARITY_ORDER = list(WORKLOADS)
 
