@@ -58,7 +58,8 @@ class Oracle:
         q: [B,H,Nq,D]; k, v: [B,H,Nk,D] in storage form (bf16 as uint16 bits).
         `scale` is used exactly as given (pass the float32 value the GPU path receives).
         rows=None computes every row in order.  window=w keeps only keys with |i - j| <= w
-        (None: no window).
+        (None: no window).  causal: False/0, True/1 (top-left, j <= i) or 2 (bottom-right,
+        j <= i + L_b - Nq: the queries are the last Nq positions of the key sequence).
         """
         q = _as_storage(q, dtype)
         k = _as_storage(k, dtype)
@@ -83,8 +84,10 @@ class Oracle:
         w = -1 if window is None else int(window)
         if w < -1:
             raise ValueError("window must be None or >= 0")
+        if int(causal) not in (0, 1, 2):
+            raise ValueError("causal must be 0, 1 or 2")
         rc = self.lib.oracle_attn_rows_window(_ptr(q), _ptr(k), _ptr(v), _CODES[dtype], B, H, Nq,
-                                              Nk, D, float(scale), int(bool(causal)), w, _ptr(kl),
+                                              Nk, D, float(scale), int(causal), w, _ptr(kl),
                                               _ptr(r), n, _ptr(o), _ptr(lse), int(nthreads))
         if rc != 0:
             raise ValueError(f"oracle_attn_rows failed with {rc}")

@@ -8,8 +8,11 @@
  *
  * What it computes (the textbook definition, not the tiled algorithm):
  *   For each batch b, head h and query row i,
- *     J(i)   = { j : 0 <= j < L_b and (not causal or j <= i)
+ *     J(i)   = { j : 0 <= j < L_b and (not causal or j <= i + c_b)
  *                    and (w < 0 or i - w <= j <= i + w) }          (masked keys excluded)
+ *   with c_b = 0 for the top-left causal mask (causal = 1) and c_b = L_b - Nq for the
+ *   bottom-right one (causal = 2: the Nq queries are the last Nq positions of a key sequence
+ *   of length L_b, as when new tokens attend to a KV cache that already holds them),
  *     s_j    = scale * sum_d q[i,d] k[j,d]                          for j in J(i)
  *     m      = max_j s_j                                            (two-pass max shift)
  *     e_j    = exp(s_j - m),  l = sum_j e_j
@@ -24,7 +27,9 @@
  *     its pitfalls list (additive -10000 mask).  Excluding masked keys equals all three
  *     fill conventions on every row that keeps at least one key.
  *   - causal mask = attend only to the current and earlier positions: hotelren.com
- *     sec.2.1 note 2; lshu.cn sec.3.1.  Read here as j <= i (top-left aligned).
+ *     sec.2.1 note 2; lshu.cn sec.3.1.  Read here as j <= i (top-left aligned); for queries
+ *     that extend a KV cache (hotelren.com sec.3.1: each new token appends its own key and
+ *     value and reuses the cached ones), query i sits at position L_b - Nq + i.
  *   - local (sliding-window) attention: each position attends only to the w positions before
  *     and after it, every other weight is zero: lshu.cn sec.2 ("localization", Longformer /
  *     BigBird windows); aicoding.csdn.net sec.4.3 (window w = 512).  Read here as the band
@@ -98,7 +103,8 @@ static void one_row(const void* q, const void* k, const void* v, int dtype, int 
         if (L > Nk) L = Nk;
     }
     int64_t jbeg = 0, jend = L; /* J(i) = [jbeg, jend) */
-    if (causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;
+    int64_t cb = causal == 2 ? L - Nq : 0;
+    if (causal && jend > (int64_t)i + cb + 1) jend = (int64_t)i + cb + 1;
     if (window >= 0) {
         if (jbeg < (int64_t)i - window) jbeg = (int64_t)i - window;
         if (jend > (int64_t)i + window + 1) jend = (int64_t)i + window + 1;
@@ -143,6 +149,7 @@ static void one_row(const void* q, const void* k, const void* v, int dtype, int 
 /*
  * oracle_attn_rows_window -- reference attention on selected query rows.
  *   q: [B,H,Nq,D], k, v: [B,H,Nk,D], contiguous, stored as `dtype` (0 fp32, 1 fp16, 2 bf16).
+ *   causal: 0 none, 1 top-left (j <= i), 2 bottom-right (j <= i + L_b - Nq).
  *   window: half-width w of the local band |i - j| <= w, or any negative value for none.
  *   key_lens: int32[B] or NULL (every key valid); values are clamped to [0, Nk].
  *   rows: flat row ids ((b*H + h)*Nq + i), or NULL for all B*H*Nq rows in order.
@@ -157,6 +164,7 @@ int oracle_attn_rows_window(const void* q, const void* k, const void* v, int dty
     if (!q || !k || !v || !o || !lse) return -1;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
     if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return -1;
+    if (causal < 0 || causal > 2) return -1;
     int64_t total = (int64_t)B * H * Nq;
     if (!rows) nrows = total;
     for (int64_t r = 0; rows && r < nrows; ++r)

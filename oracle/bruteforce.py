@@ -4,8 +4,8 @@ Pure-Python `decimal` arithmetic at 50 significant digits (Decimal.exp and Decim
 correctly rounded), so for inputs that are exact binary fractions the result is the exact
 attention output to ~1e-48.  It follows the same plain definition as attn_oracle.c but
 shares no code with it: masked keys are left out of the softmax, the causal mask keeps
-keys j <= i, a window w keeps keys with |i - j| <= w, and a row with no key gives O = 0 and
-LSE = -inf.
+keys j <= i (causal = 2: j <= i + L_b - Nq, the queries being the last Nq positions), a window
+w keeps keys with |i - j| <= w, and a row with no key gives O = 0 and LSE = -inf.
 """
 from __future__ import annotations
 
@@ -59,9 +59,10 @@ def attention(q, k, v, scale, causal=False, key_lens=None, digits: int = 50, win
             Nk = len(k[b][h])
             kb = Nk if key_lens is None else max(0, min(Nk, int(key_lens[b])))
             oh, lh = [], []
+            shift = kb - len(q[b][h]) if causal == 2 else 0
             for i, qr in enumerate(q[b][h]):
                 keep = [j for j in range(kb)
-                        if (not causal or j <= i) and (window is None or abs(i - j) <= window)]
+                        if (not causal or j <= i + shift) and (window is None or abs(i - j) <= window)]
                 o, lse = attention_row(qr, [k[b][h][j] for j in keep], [v[b][h][j] for j in keep],
                                        scale, digits)
                 oh.append(o)

@@ -45,6 +45,8 @@ CASES = [
     ("window2_causal_q6_k6_d3", 1, 1, 6, 6, 3, 0.5, True, None, 2),
     ("window0_q4_k5_d2", 1, 1, 4, 5, 2, 1.0, False, None, 0),
     ("window1_padded_lens_4_2_q5_k6_d2", 2, 1, 5, 6, 2, 0.5, False, [4, 2], 1),
+    ("bottomright_q2_k5_d2", 1, 1, 2, 5, 2, 0.5, 2, None, None),
+    ("bottomright_padded_lens_4_1_q3_k6_d2", 2, 1, 3, 6, 2, 1.0, 2, [4, 1], None),
 ]
 
 

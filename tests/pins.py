@@ -358,6 +358,55 @@ def pin_torch_sdpa_window(impl):
                 close(lse[live], rl[live], 1e-13, f"sdpa window={window} lse {dtype} causal={causal}")
 
 
+def pin_bottom_right_causal(impl):
+    """Queries that are the last Nq positions of the key sequence (a KV cache): one query sees
+    every valid key (the unmasked result, bit for bit); Nq = Nk without padding is the top-left
+    mask; Q = 0 gives the mean over keys 0 .. i + L_b - Nq; torch agrees with an explicit mask."""
+    rng = np.random.default_rng(25)
+    for dtype in ("f32", "bf16"):
+        B, H, Nk, D = 3, 2, 11, 8
+        k = rand_store(rng, (B, H, Nk, D), dtype)
+        v = rand_store(rng, (B, H, Nk, D), dtype)
+        kl = np.array([11, 6, 0], np.int32)
+        q1 = rand_store(rng, (B, H, 1, D), dtype)
+        a = impl.attn(q1, k, v, dtype, 0.3, 2, kl)
+        b = impl.attn(q1, k, v, dtype, 0.3, 0, kl)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "one query sees the cache"
+        qs = rand_store(rng, (B, H, Nk, D), dtype)
+        a = impl.attn(qs, k, v, dtype, 0.3, 2)
+        b = impl.attn(qs, k, v, dtype, 0.3, 1)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "square: top-left"
+        Nq = 4
+        q0 = store(np.zeros((B, H, Nq, D)), dtype)
+        o, lse = impl.attn(q0, k, v, dtype, 0.3, 2, kl)
+        vd = storage_to_f64(v, dtype)
+        for bb in range(B):
+            L = int(kl[bb])
+            for i in range(Nq):
+                n = max(0, min(L, i + L - Nq + 1))
+                if n == 0:
+                    assert np.all(o[bb, :, i] == 0) and np.all(lse[bb, :, i] == -np.inf)
+                    continue
+                close(o[bb, :, i], vd[bb, :, :n].mean(axis=1), 1e-14, "bottom-right Q=0 mean")
+                close(lse[bb, :, i], np.full(H, math.log(n)), 1e-14, "bottom-right Q=0 lse")
+        import torch
+        qq = rand_store(rng, (B, H, Nq, D), dtype)
+        o, lse = impl.attn(qq, k, v, dtype, 0.3, 2, kl)
+        qd, kd, vd2 = (torch.from_numpy(storage_to_f64(t, dtype)) for t in (qq, k, v))
+        i = torch.arange(Nq)[:, None]
+        j = torch.arange(Nk)[None, :]
+        L = torch.from_numpy(kl.astype(np.int64))[:, None, None]
+        allow = ((j < L) & (j <= i + L - Nq))[:, None]
+        s = torch.matmul(qd, kd.transpose(-2, -1)) * 0.3
+        s = s.masked_fill(~allow, float("-inf"))
+        rl = torch.logsumexp(s, dim=-1).numpy()
+        ro = torch.nn.functional.scaled_dot_product_attention(qd, kd, vd2, attn_mask=allow, scale=0.3).numpy()
+        live = np.isfinite(rl)
+        close(o[live], ro[live], 1e-13, "bottom-right vs torch O")
+        close(lse[live], rl[live], 1e-13, "bottom-right vs torch lse")
+        assert np.all(lse[~live] == -np.inf)
+
+
 def window_set(i, L, causal, w):
     """The keys row i may attend to, written out from the band's definition |i - j| <= w."""
     return [j for j in range(L) if (not causal or j <= i) and abs(i - j) <= w]
@@ -451,6 +500,6 @@ ALL_PINS = [
     pin_zero_query_mean, pin_scale_zero, pin_causal_row0, pin_single_key, pin_two_keys,
     pin_one_hot_dominant, pin_huge_logit_gap, pin_empty_rows, pin_rows_sum_to_one,
     pin_permutations, pin_key_shift, pin_chunked_lse, pin_torch_sdpa_small,
-    pin_torch_sdpa_window, pin_window_zero_query_mean, pin_window_extremes,
+    pin_torch_sdpa_window, pin_window_zero_query_mean, pin_window_extremes, pin_bottom_right_causal,
     pin_golden_bruteforce, pin_decoders,
 ]

@@ -212,6 +212,8 @@ def test_kernel_golden_bruteforce():
     with open(os.path.join(os.path.dirname(__file__), "golden", "bruteforce_tiny.json")) as f:
         cases = json.load(f)["cases"]
     for cs in cases:
+        if cs["causal"] == 2:
+            continue  # queries at the end of a KV cache: attn_decode's cases (test_gpu_decode.py)
         for dtype in ("bf16", "f16", "f32"):
             D = cs["D"]
             pad = lambda a: np.pad(np.array(a, np.float64), [(0, 0)] * 3 + [(0, 64 - D)])

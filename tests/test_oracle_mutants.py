@@ -18,8 +18,8 @@ MUTANTS = [
     ("missing normalisation", "for (int d = 0; d < D; ++d) o[d] /= l;", ""),
     ("log2 in the LSE", "*lse = m + log(l);", "*lse = m + log2(l);"),
     ("LSE without the max", "*lse = m + log(l);", "*lse = log(l);"),
-    ("causal j < i", "jend = (int64_t)i + 1;", "jend = (int64_t)i;"),
-    ("causal ignored", "if (causal && jend > (int64_t)i + 1)", "if (0 && jend > (int64_t)i + 1)"),
+    ("causal j < i", "jend = (int64_t)i + cb + 1;", "jend = (int64_t)i + cb;"),
+    ("causal ignored", "if (causal && jend > (int64_t)i + cb + 1)", "if (0 && jend > (int64_t)i + cb + 1)"),
     ("key lengths ignored", "L = key_lens[b];", "L = Nk;"),
     ("key length off by one", "L = key_lens[b];", "L = key_lens[b] - 1;"),
     ("batch index from head", "int b = (int)(bh / H);", "int b = (int)(bh % H);"),
@@ -34,6 +34,9 @@ MUTANTS = [
     ("window start off by one", "jbeg = (int64_t)i - window;", "jbeg = (int64_t)i - window + 1;"),
     ("window start ignored", "if (jbeg < (int64_t)i - window) jbeg = (int64_t)i - window;", ""),
     ("window end off by one", "jend = (int64_t)i + window + 1;", "jend = (int64_t)i + window;"),
+    ("bottom-right shift ignored", "int64_t cb = causal == 2 ? L - Nq : 0;", "int64_t cb = 0;"),
+    ("bottom-right shift from Nk", "int64_t cb = causal == 2 ? L - Nq : 0;", "int64_t cb = causal == 2 ? Nk - Nq : 0;"),
+    ("bottom-right off by one", "int64_t cb = causal == 2 ? L - Nq : 0;", "int64_t cb = causal == 2 ? L - Nq - 1 : 0;"),
     ("window end ignored", "if (jend > (int64_t)i + window + 1) jend = (int64_t)i + window + 1;", ""),
     ("empty row LSE 0", "*lse = -INFINITY;", "*lse = 0.0;"),
     ("bf16 shift 15", "uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
