@@ -3,7 +3,8 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
-resident in HBM).  W untimed warm-up steps, then K timed steps bracketed by device
+resident in HBM; attn_decode, key splits and merge, for the KV-cache decode workloads, whose
+line reports HBM GB/s against the 8 TB/s peak instead of TFLOP/s).  W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation, timed with HIP events recorded on the stream the kernel is launched on.
 Prints ONE JSON line on stdout (everything else goes to stderr).
 
@@ -27,10 +28,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·D, causal halved) and % of bf16 MFMA peak"
 METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4·D per (query, key) pair inside the band)"
+METRIC_DECODE = "KV-cache decode attention HBM GB/s (Q, valid K/V rows, O and LSE bytes per step)"
 # MI355X published dense peaks (256 CUs at 2.4 GHz).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["attn_common.h", "attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+KERNEL_SOURCES = ["attn_common.h", "attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
 
 
 def log(*a):
@@ -59,9 +61,18 @@ def read_traffic(workload: str, src_hash: str):
     return float(m_bytes.group(1))
 
 
-def algorithmic_bytes(w) -> float:
+def algorithmic_bytes(w, key_lens=None) -> float:
+    """Bytes one step must move at least: Q and O, K and V once (their valid rows when key
+    lengths are given), LSE in fp32."""
     eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
-    return eb * (2 * w.B * w.H * w.Nq * w.D + 2 * w.B * w.H * w.Nk * w.D) + 4 * w.B * w.H * w.Nq
+    kv_rows = w.B * w.Nk if key_lens is None else \
+        int(sum(min(max(int(n), 0), w.Nk) for n in key_lens))
+    return eb * (2 * w.B * w.H * w.Nq * w.D + 2 * w.H * kv_rows * w.D) + 4 * w.B * w.H * w.Nq
+
+
+def oracle_causal(w) -> int:
+    """The oracle's mask code: 2 puts the queries at the end of each key sequence."""
+    return 2 if (w.causal and w.kv_cache) else int(w.causal)
 
 
 def row_pairs(w, rows, key_lens):
@@ -72,6 +83,8 @@ def row_pairs(w, rows, key_lens):
     b = rows // (w.H * w.Nq)
     L = np.full(rows.shape, w.Nk, dtype=np.int64) if key_lens is None else \
         np.clip(key_lens.astype(np.int64), 0, w.Nk)[b]
+    if w.kv_cache:
+        return np.clip(i + 1 + L - w.Nq, 0, L) if w.causal else L
     hi = np.minimum(L, i + 1) if w.causal else L
     if w.window is None:
         return hi
@@ -90,7 +103,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
     cores = impl.max_threads()
     rng = np.random.default_rng(seed)
     total = w.B * w.H * w.Nq
-    args = (x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), w.causal, x["key_lens"])
+    args = (x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), oracle_causal(w), x["key_lens"])
 
     # Size the sample from a timed pilot, growing it until it covers at least half the target.
     n = 256
@@ -103,7 +116,15 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
         if dt >= 0.5 * target_s or n >= total:
             break
         n = int(n * min(64.0, max(2.0, target_s / max(dt, 1e-3))))
-    flops = 4.0 * w.D * float(row_pairs(w, rows, x["key_lens"]).sum())
+    reps = 1
+    if n >= total and dt < 0.5 * target_s:  # the whole workload is small: time repeats of it
+        reps = max(1, int(0.5 * target_s / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            ro, rl = impl.attn_rows(*args, rows=rows, window=w.window)
+        dt = (time.perf_counter() - t0) / reps
+    pairs = float(row_pairs(w, rows, x["key_lens"]).sum())
+    flops = 4.0 * w.D * pairs
 
     D = w.D
     o = o_dev.detach().reshape(-1, D)[torch.from_numpy(rows).to(o_dev.device)].double().cpu().numpy()
@@ -111,14 +132,22 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
     fin = np.isfinite(rl)
     err_o = float(np.max(np.abs(o - ro)))
     err_l = float(np.max(np.abs(lse[fin] - rl[fin]))) if fin.any() else 0.0
+    if w.kv_cache:  # the metric's unit: the step's algorithmic bytes, prorated by visible pairs
+        all_rows = np.arange(total, dtype=np.int64)
+        share = pairs / max(float(row_pairs(w, all_rows, x["key_lens"]).sum()), 1.0)
+        value, unit = algorithmic_bytes(w, x["key_lens"]) * share / dt / 1e9, "GB/s"
+        counted = "bytes counted as the step's algorithmic bytes times the sample's share of the " \
+                  "visible (query, key) pairs, as in the metric"
+    else:
+        value, unit = flops / dt / 1e12, "TFLOP/s"
+        counted = "flops counted as 4*D per valid (query, key) pair, as in the metric"
     return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
+        "value": value,
+        "unit": unit,
         "cores": cores,
         "kind": "oracle",
         "sample": f"{rows.size} random query rows of the same workload (seed {seed}), fp64 oracle "
-                  f"with {cores} OpenMP threads, {dt:.2f} s; flops counted as 4*D per valid "
-                  f"(query, key) pair, as in the metric",
+                  f"with {cores} OpenMP threads, {dt:.3f} s per pass ({reps} passes); {counted}",
         "seconds": dt,
         "sample_max_abs_err_o": err_o,
         "sample_max_abs_err_lse": err_l,
@@ -174,9 +203,18 @@ def main():
     stream = torch.cuda.current_stream(dev)
     scale = float(x["scale"])
 
-    def step():
-        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream,
-                    window=w.window)
+    if w.kv_cache:
+        ws_bytes = binding.attn_decode_workspace_size(w.B, w.H, w.Nq, w.Nk, w.D, inputs.DTYPE_CODE[w.dtype])
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        log(f"[bench] decode workspace {ws_bytes} bytes")
+
+        def step():
+            binding.decode(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse,
+                           workspace=workspace, stream=stream)
+    else:
+        def step():
+            binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse,
+                        stream=stream, window=w.window)
 
     for _ in range(a.warmup):
         step()
@@ -216,17 +254,31 @@ def main():
         del src, dst
 
     flops = w.flops()
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     traffic = read_traffic(name, src_hash)
-    abytes = algorithmic_bytes(w)
+    abytes = algorithmic_bytes(w, x["key_lens"])
+    if w.kv_cache:
+        # HBM-bound: K and V are read once and each byte feeds 2 flops per query.
+        metric, unit = METRIC_DECODE, "GB/s"
+        value = abytes / (ms_per_step * 1e-3) / 1e9
+        achieved = abytes / (avg_launch_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                    "kernels": "attn_fwd_mfma_kernel (key splits) + attn_merge_kernel, timed together"}
+        peak = PEAK_HBM_GBS
+    else:
+        metric, unit = (METRIC if w.window is None else METRIC_WINDOW), "TFLOP/s"
+        value = tflops
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": traffic}
 
     result = {
-        "metric": METRIC if w.window is None else METRIC_WINDOW,
+        "metric": metric,
         "value": value,
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
@@ -237,11 +289,11 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
-                   "causal": w.causal, "key_padding": w.padded, "window": w.window, "seed": x["seed"],
-                   "parallelism": "none (1 GPU)"},
+                   "causal": w.causal, "key_padding": w.padded, "window": w.window,
+                   "kv_cache": w.kv_cache, "seed": x["seed"], "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic},
+        "roofline": roofline,
+        "tflops": tflops,
         "avg_launch_ms": avg_launch_ms,
         "algorithmic_bytes": abytes,
         "algorithmic_gbs": abytes / (avg_launch_ms * 1e-3) / 1e9,
@@ -252,7 +304,7 @@ def main():
         log(f"[bench] cpu baseline: oracle on a sample (~{a.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, x, o, lse, a.cpu_seconds)
         cb = result["cpu_baseline"]
-        log(f"[bench] cpu baseline {cb['value'] * 1e3:.3f} GFLOP/s on {cb['cores']} threads; "
+        log(f"[bench] cpu baseline {cb['value']:.4g} {cb['unit']} on {cb['cores']} threads; "
             f"sample max|dO|={cb['sample_max_abs_err_o']:.3e} max|dLSE|={cb['sample_max_abs_err_lse']:.3e}")
     else:
         result["cpu_baseline"] = None

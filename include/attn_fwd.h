@@ -26,6 +26,7 @@
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -49,7 +50,8 @@ typedef enum {
     ATTN_ERR_FLAG = -6,     /* causal is not 0 or 1 */
     ATTN_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
     ATTN_ERR_ALIGN = -8,    /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
-    ATTN_ERR_WINDOW = -9    /* window is below -1 (attn_fwd_window) */
+    ATTN_ERR_WINDOW = -9,   /* window is below -1 (attn_fwd_window) */
+    ATTN_ERR_WORKSPACE = -10 /* workspace smaller than attn_decode_workspace_size() (attn_decode) */
 } attn_status;
 
 /*
@@ -102,6 +104,39 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int H, int Nq, int Nk, int D, float scale, int causal, int window,
                     const int32_t* key_lens, int dtype, void* stream);
+
+/*
+ * attn_decode -- attention of Nq new queries against a KV cache: the queries are the last Nq
+ * positions of each cached sequence (the cache already holds their own keys and values), so
+ * with causal = 1 query i keeps keys j <= i + L_b - Nq (bottom-right aligned), and with one
+ * query every valid key.  Source: the KV cache that keeps every token's key and value and lets
+ * each new token reuse them instead of recomputing the sequence (hotelren.com page, sec.3.1).
+ *
+ * Made for small Nq and long Nk: the keys of each (query tile, b, h) are split over several
+ * workgroups so that even B*H = 32 fills the chip; each split writes an fp32 partial result (O
+ * over its keys, its log-sum-exp) to `workspace`, and a second kernel on the same stream merges
+ * them: LSE = ln sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.  When one split is enough no
+ * workspace is used.  Otherwise identical to attn_fwd (layouts, key_lens, dtypes, scale, O
+ * rounding, empty rows give O = 0 and LSE = -inf).
+ *
+ *   causal           0: every valid key; 1: bottom-right causal mask as above.
+ *   workspace        device memory of at least attn_decode_workspace_size(B, H, Nq, Nk, D, dtype)
+ *                    bytes, 16-byte aligned, owned by the caller (may be NULL when that size is
+ *                    0); its contents on entry do not matter, and it is overwritten.
+ *   workspace_bytes  its size.
+ * Errors as attn_fwd, plus ATTN_ERR_NULL / ATTN_ERR_ALIGN for a missing or misaligned
+ * workspace and ATTN_ERR_WORKSPACE when it is too small; nothing is enqueued on any error.
+ * Calls that share a workspace must not overlap in time.
+ */
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_workspace_size -- bytes of workspace attn_decode needs for these sizes (0 when it
+ * needs none, or when the sizes are invalid).  A pure function of its arguments.
+ */
+size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D, int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);

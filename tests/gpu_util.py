@@ -39,6 +39,16 @@ def run(x: dict, dtype: str, causal: bool, scale=None, dev="cuda", window=None):
     return o, lse
 
 
+def run_decode(x: dict, dtype: str, causal: bool, scale=None, dev="cuda", workspace=None):
+    """attn_decode through the binding: the queries are the last Nq positions of each cache."""
+    q, k, v = (to_device(x[n], dtype, dev) for n in "qkv")
+    kl = None if x.get("key_lens") is None else torch.from_numpy(np.asarray(x["key_lens"], np.int32)).to(dev)
+    s = float(x["scale"]) if scale is None else float(scale)
+    o, lse = binding.decode(q, k, v, causal=causal, key_lens=kl, scale=s, workspace=workspace)
+    torch.cuda.synchronize()
+    return o, lse
+
+
 def compare(o_dev, lse_dev, o_ref, lse_ref, dtype, what="", rows=None):
     """Max-abs comparison; -inf / non-finite patterns must be identical.  Returns the errors."""
     o = to_f64(o_dev)

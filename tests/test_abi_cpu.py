@@ -96,3 +96,43 @@ def test_package_import_loads_nothing():
             "print(binding._lib is None)") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "True"
+
+
+DECODE_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=1, Nk=4096, D=64, scale=0.125,
+                 causal=1, key_lens=None, dtype=2, ws=FAKE, ws_bytes=1 << 20, stream=None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(B=0), -2), (dict(D=96), -3), (dict(dtype=5), -4),
+    (dict(scale=float("inf")), -5), (dict(causal=2), -6), (dict(lse=FAKE + 4), -8),
+    (dict(ws=None), -1), (dict(ws=FAKE + 8), -8), (dict(ws_bytes=0), -10), (dict(ws_bytes=4159), -10),
+])
+def test_host_validation_decode(over, code):
+    """attn_decode rejects bad arguments and a missing, misaligned or short workspace on the host
+    (B=H=Nq=1, Nk=4096, D=64 spreads the keys over 16 splits: 16 * (64 + 1) * 4 = 4160 bytes)."""
+    a = dict(DECODE_OK)
+    a.update(over)
+    rc = binding.attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                             a["Nk"], a["D"], a["scale"], a["causal"], a["key_lens"], a["dtype"],
+                             a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code
+
+
+def test_decode_workspace_size():
+    """The workspace holds n_splits fp32 copies of O and LSE: n_splits * B*H*Nq * (D + 1) * 4
+    bytes, with at most 64 splits of at least 256 keys; 0 when the cache is not split, or for
+    arguments attn_decode would reject."""
+    ws = binding.attn_decode_workspace_size
+    assert ws(1, 1, 1, 4096, 64, 2) == 16 * 65 * 4
+    assert ws(1, 1, 1, 511, 128, 2) == 0          # below two 256-key splits
+    assert ws(1, 1, 1, 512, 128, 2) == 2 * 129 * 4
+    assert ws(64, 32, 1, 1 << 20, 128, 2) == 0    # 2048 workgroups without a split
+    for B, H, Nq, Nk, D, dt in ((1, 32, 1, 32768, 128, 2), (4, 32, 1, 4096, 128, 2),
+                                (16, 32, 1, 8192, 128, 1), (2, 8, 200, 70000, 64, 0)):
+        n = ws(B, H, Nq, Nk, D, dt)
+        unit = B * H * Nq * (D + 1) * 4
+        assert n % unit == 0 and 2 <= n // unit <= 64, (B, H, Nq, Nk, D, n)
+        assert n // unit <= Nk // 256
+    for bad in ((0, 1, 1, 4096, 64, 2), (1, 1, 1, 4096, 80, 2), (1, 1, 1, 4096, 64, 7),
+                (1, 1, 0, 4096, 64, 2)):
+        assert ws(*bad) == 0

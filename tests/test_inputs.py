@@ -100,3 +100,28 @@ def test_band_pair_count():
                         if abs(i - j) <= w and (not causal or j <= i))
             assert wl.band_pairs() == brute
             assert wl.flops() == 4.0 * 2 * 3 * 64 * brute
+
+
+def test_cache_pair_count():
+    """A KV-cache step's FLOP count is 4*B*H*D times the visible pairs: query i is position
+    Nk - Nq + i of the sequence and sees keys j <= Nk - Nq + i when causal (brute force)."""
+    for causal in (False, True):
+        for nq, nk in ((1, 1), (1, 50), (7, 50), (50, 50), (60, 50)):
+            wl = inputs.Workload("t", "bf16", 2, 3, nq, nk, 64, causal, False, 1.0, 1.0, 1, kv_cache=True)
+            brute = sum(1 for i in range(nq) for j in range(nk) if not causal or j <= nk - nq + i)
+            assert wl.cache_pairs() == brute
+            assert wl.flops() == 4.0 * 2 * 3 * 64 * brute
+    w = inputs.WORKLOADS["kvdecode_bf16_b1h32q1k16384d128"]
+    assert w.flops() == 4.0 * 32 * 128 * 16384
+
+
+def test_key_length_range():
+    """Key lengths cover [lo, Nk] inclusive; the BERT-like batch keeps [64, 512]."""
+    kl = inputs.make_key_lens(3, 20000, 40, 30)
+    assert kl.min() == 30 and kl.max() == 40 and len(np.unique(kl)) == 11
+    assert np.array_equal(inputs.make_key_lens(3, 32), inputs.make_key_lens(3, 32, 512, 64))
+    w = inputs.WORKLOADS["kvdecode_ragged_bf16_b16h32q1k8192d128"]
+    kl = inputs.make_key_lens(w.seed, w.B, w.Nk, w.len_lo)
+    assert kl.shape == (16,) and kl.min() >= 1024 and kl.max() <= 8192
+    with pytest.raises(ValueError):
+        inputs.make_key_lens(1, 4, 10, 11)

@@ -1,9 +1,10 @@
 """Python binding of the C ABI in include/attn_fwd.h (argument marshalling only).
 
-`attn_fwd`, `attn_fwd_window` and `attn_status_str` mirror the C entry points one to one (raw
-device pointers, sizes, a stream handle).  `fwd` is the tensor-level convenience: it checks the
-tensors on the host, allocates O and LSE with torch on the current stream and calls
-`attn_fwd` (or `attn_fwd_window` when a local window is asked for).  Every step of
+`attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size` and
+`attn_status_str` mirror the C entry points one to one (raw device pointers, sizes, a stream
+handle).  `fwd` and `decode` are the tensor-level conveniences: they check the tensors on the
+host, allocate O, LSE (and the decode workspace) with torch on the current stream and call
+`attn_fwd` / `attn_fwd_window` / `attn_decode`.  Every step of
 the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
 module raises instead of computing anything itself.
 """
@@ -21,9 +22,10 @@ ATTN_OK = 0
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_FLAG", -7: "ATTN_ERR_LAUNCH",
-    -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW",
+    -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size",
+           "attn_status_str")
 
 _lib = None
 
@@ -55,6 +57,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
     ]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p,
+    ]
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -72,6 +83,17 @@ def attn_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window, key
     """The C entry point with a local band |i - j| <= window (-1: no band)."""
     return load_library().attn_fwd_window(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, window,
                                           key_lens, dtype, stream)
+
+
+def attn_decode(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, workspace,
+                workspace_bytes, stream) -> int:
+    """The C entry point for queries at the end of a KV cache (key split + merge)."""
+    return load_library().attn_decode(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens,
+                                      dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_workspace_size(B, H, Nq, Nk, D, dtype) -> int:
+    return int(load_library().attn_decode_workspace_size(B, H, Nq, Nk, D, dtype))
 
 
 def attn_status_str(status: int) -> str:
@@ -92,12 +114,8 @@ def dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None, out=None,
-        lse=None, stream=None, window: int | None = None):
-    """O, LSE = attention(q, k, v).  q: [B,H,Nq,D]; k, v: [B,H,Nk,D]; all contiguous CUDA tensors
-    of one dtype; key_lens: int32 [B] on the same device or None.  scale defaults to 1/sqrt(D).
-    window=w keeps only keys with |i - j| <= w (sliding-window attention); None: every key.
-    Returns O (q's dtype, [B,H,Nq,D]) and LSE (float32, [B,H,Nq])."""
+def _check(q, k, v, key_lens, scale, out, lse, stream):
+    """Host checks shared by fwd and decode; returns the marshalled arguments."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -123,8 +141,6 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
         scale = 1.0 / math.sqrt(D)
     if not math.isfinite(scale):
         raise ValueError("scale must be finite")
-    if window is not None and (int(window) != window or window < 0):
-        raise ValueError("window must be None or an integer >= 0")
     kl_ptr = None
     if key_lens is not None:
         if (not isinstance(key_lens, torch.Tensor) or key_lens.dtype != torch.int32
@@ -144,12 +160,52 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return B, H, Nq, Nk, D, code, float(scale), kl_ptr, out, lse, handle
+
+
+def decode(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None, out=None,
+           lse=None, workspace=None, stream=None):
+    """O, LSE for Nq new queries that are the last Nq positions of each cached sequence.
+    q: [B,H,Nq,D]; k, v: [B,H,Nk,D] (the cache, already holding the new tokens' keys and
+    values); key_lens: int32 [B] valid cache lengths or None.  causal=True keeps, for query i,
+    the keys j <= i + L_b - Nq.  workspace: a CUDA tensor of at least
+    attn_decode_workspace_size(...) bytes, or None to allocate one with torch."""
+    torch = _torch()
+    B, H, Nq, Nk, D, code, scale, kl_ptr, out, lse, handle = _check(q, k, v, key_lens, scale, out,
+                                                                  lse, stream)
+    need = attn_decode_workspace_size(B, H, Nq, Nk, D, code)
+    ws_ptr, ws_bytes = None, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device \
+                or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    rc = attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, Nq, Nk, D, scale, int(bool(causal)), kl_ptr, code, ws_ptr, ws_bytes,
+                     handle)
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return out, lse
+
+
+def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = None, out=None,
+        lse=None, stream=None, window: int | None = None):
+    """O, LSE = attention(q, k, v).  q: [B,H,Nq,D]; k, v: [B,H,Nk,D]; all contiguous CUDA tensors
+    of one dtype; key_lens: int32 [B] on the same device or None.  scale defaults to 1/sqrt(D).
+    window=w keeps only keys with |i - j| <= w (sliding-window attention); None: every key.
+    Returns O (q's dtype, [B,H,Nq,D]) and LSE (float32, [B,H,Nq])."""
+    if window is not None and (int(window) != window or window < 0):
+        raise ValueError("window must be None or an integer >= 0")
+    B, H, Nq, Nk, D, code, scale, kl_ptr, out, lse, handle = _check(q, k, v, key_lens, scale, out,
+                                                                  lse, stream)
     if window is None:
         rc = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, Nq, Nk, D, float(scale), int(bool(causal)), kl_ptr, code, handle)
+                      B, H, Nq, Nk, D, scale, int(bool(causal)), kl_ptr, code, handle)
     else:
         rc = attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             lse.data_ptr(), B, H, Nq, Nk, D, float(scale), int(bool(causal)),
+                             lse.data_ptr(), B, H, Nq, Nk, D, scale, int(bool(causal)),
                              min(int(window), 2**31 - 1), kl_ptr, code, handle)
     if rc != ATTN_OK:
         raise AttnError(rc)

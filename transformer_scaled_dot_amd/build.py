@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_fwd.so")
-SOURCES = ["attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip"]
+SOURCES = ["attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
 HEADERS = ["attn_common.h", os.path.join(ROOT, "include", "attn_fwd.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

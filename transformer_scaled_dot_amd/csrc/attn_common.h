@@ -20,8 +20,31 @@ struct Params {
     float scale_log2;  // max(|scale| * log2(e), 1e-30): logits are handled in base-2 units
     int negate_q;      // scale < 0: the sign is moved onto Q (an exact bit flip)
     int causal;
+    int causal_br;     // causal mask aligned bottom-right: query i keeps keys j <= i + L_b - Nq
     int window;        // half-width w of the local band |i - j| <= w, or -1 for none
+    // Key-range split: each (Q tile, b, h) is spread over n_splits workgroups, split s taking
+    // keys [s * split_len, (s + 1) * split_len).  With n_splits > 1 the workgroups write fp32
+    // partial results (O normalised over the split's keys, LSE of the split) to o_part
+    // [n_splits, B, H, Nq, D] and lse_part [n_splits, B, H, Nq]; a merge kernel combines them.
+    int n_splits;
+    int split_len;
+    float* o_part;
+    float* lse_part;
 };
+
+// Which (split, b*H + h, Q tile) a workgroup owns; splits of one Q tile are adjacent in the
+// logical order.
+struct BlockWork {
+    int split, bh, qt;
+};
+__device__ __forceinline__ BlockWork block_work(const Params& p, int blk) {
+    BlockWork w;
+    w.split = blk % p.n_splits;
+    const int rest = blk / p.n_splits;
+    w.bh = rest / p.n_qtiles;
+    w.qt = rest - w.bh * p.n_qtiles;
+    return w;
+}
 
 // Keys [lo, hi) that row i may attend to, before the padding length: the causal rule keeps
 // j <= i, the local band keeps |i - j| <= w.
@@ -30,7 +53,7 @@ __device__ __forceinline__ int row_key_lo(const Params& p, int i) {
 }
 __device__ __forceinline__ int row_key_hi(const Params& p, int i, int kv_valid) {
     int hi = kv_valid;
-    if (p.causal) hi = min(hi, i + 1);
+    if (p.causal) hi = min(hi, i + 1 + (p.causal_br ? kv_valid - p.Nq : 0));
     if (p.window >= 0) hi = min(hi, i + p.window + 1);
     return hi;
 }
@@ -57,5 +80,6 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // Launchers, one per kernel family (defined in their .hip files).
 hipError_t attn_launch_mfma(const attn::Params& p, int dtype, int D, hipStream_t stream);
 hipError_t attn_launch_f32(const attn::Params& p, int D, hipStream_t stream);
+hipError_t attn_launch_merge(const attn::Params& p, int dtype, int D, hipStream_t stream);
 int attn_mfma_block_m();
 int attn_f32_block_m();

@@ -5,16 +5,19 @@
 #include <attn_fwd.h>
 #include "attn_common.h"
 
-extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Nq, int Nk, int D, float scale, int causal,
-                               int window, const int32_t* key_lens, int dtype, void* stream) {
+namespace {
+
+// Checks shared by every entry point and the parameters they have in common.  Returns
+// ATTN_OK and fills p, or the first error found (nothing is enqueued then).
+int prepare(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+            int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+            attn::Params& p) {
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
-    if (window < -1) return ATTN_ERR_WINDOW;
     if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) != 0 ||
         ((uintptr_t)key_lens & 3) != 0)
         return ATTN_ERR_ALIGN;
@@ -27,7 +30,6 @@ extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void
     const int64_t n_blocks = n_qtiles * H * B;
     if (n_blocks > INT32_MAX) return ATTN_ERR_SHAPE;
 
-    attn::Params p;
     p.q = q;
     p.k = k;
     p.v = v;
@@ -47,12 +49,93 @@ extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void
     p.scale_log2 = (float)fmax(fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate_q = scale < 0.f;
     p.causal = causal;
+    p.causal_br = 0;
+    p.window = -1;
+    p.n_splits = 1;
+    p.split_len = 0;
+    p.o_part = nullptr;
+    p.lse_part = nullptr;
+    return ATTN_OK;
+}
+
+hipError_t launch(const attn::Params& p, int dtype, int D, hipStream_t s) {
+    return dtype == ATTN_F32 ? attn_launch_f32(p, D, s) : attn_launch_mfma(p, dtype, D, s);
+}
+
+// How a decode call spreads the keys over workgroups: enough splits to give the chip about
+// 2048 workgroups, at most 64, each split at least four 64-key tiles long.  A pure function of
+// the sizes, so the workspace query and the call always agree.
+struct DecodePlan {
+    int n_splits;
+    int split_len;
+    size_t workspace_bytes;
+};
+
+DecodePlan decode_plan(int B, int H, int Nq, int Nk, int D, int dtype) {
+    const int bm = dtype == ATTN_F32 ? attn_f32_block_m() : attn_mfma_block_m();
+    const int64_t base = (int64_t)B * H * (((int64_t)Nq + bm - 1) / bm);
+    int64_t S = (2048 + base - 1) / base;
+    S = S < 64 ? S : 64;
+    const int64_t by_len = Nk / 256;
+    S = S < by_len ? S : by_len;
+    if (S < 1) S = 1;
+    DecodePlan plan{1, 0, 0};
+    if (S == 1) return plan;
+    const int64_t len = ((Nk + S - 1) / S + 63) / 64 * 64;
+    plan.split_len = (int)len;
+    plan.n_splits = (int)((Nk + len - 1) / len);
+    if (plan.n_splits > 1)
+        plan.workspace_bytes = (size_t)plan.n_splits * B * H * Nq * (size_t)(D + 1) * sizeof(float);
+    else
+        plan.split_len = 0;
+    return plan;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                               int window, const int32_t* key_lens, int dtype, void* stream) {
+    attn::Params p;
+    const int rc = prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, p);
+    if (rc != ATTN_OK) return rc;
+    if (window < -1) return ATTN_ERR_WINDOW;
     // |i - j| < max(Nq, Nk) always holds: a band at least that wide is no band.
     p.window = window >= (Nq > Nk ? Nq : Nk) ? -1 : window;
+    return launch(p, dtype, D, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
 
+extern "C" size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D, int dtype) {
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (D != 64 && D != 128) ||
+        (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16))
+        return 0;
+    return decode_plan(B, H, Nq, Nk, D, dtype).workspace_bytes;
+}
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Nq, int Nk, int D, float scale, int causal,
+                           const int32_t* key_lens, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    attn::Params p;
+    const int rc = prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, p);
+    if (rc != ATTN_OK) return rc;
+    p.causal_br = 1;  // the queries are the last Nq positions of each cached sequence
+    const DecodePlan plan = decode_plan(B, H, Nq, Nk, D, dtype);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = dtype == ATTN_F32 ? attn_launch_f32(p, D, s) : attn_launch_mfma(p, dtype, D, s);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    if (plan.n_splits == 1) return launch(p, dtype, D, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+
+    if (!workspace) return ATTN_ERR_NULL;
+    if (((uintptr_t)workspace & 15) != 0) return ATTN_ERR_ALIGN;
+    if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
+    const int64_t n_blocks = (int64_t)p.n_blocks * plan.n_splits;
+    if (n_blocks > INT32_MAX || (int64_t)B * H * Nq > INT32_MAX) return ATTN_ERR_SHAPE;
+    p.n_blocks = (int)n_blocks;
+    p.n_splits = plan.n_splits;
+    p.split_len = plan.split_len;
+    p.o_part = (float*)workspace;
+    p.lse_part = p.o_part + (size_t)plan.n_splits * B * H * Nq * D;
+    if (launch(p, dtype, D, s) != hipSuccess) return ATTN_ERR_LAUNCH;
+    return attn_launch_merge(p, dtype, D, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -74,6 +157,7 @@ extern "C" const char* attn_status_str(int status) {
         case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned, key_lens 4-byte aligned";
         case ATTN_ERR_WINDOW: return "window must be -1 (no band) or >= 0";
+        case ATTN_ERR_WORKSPACE: return "workspace_bytes is below attn_decode_workspace_size()";
         default: return "unknown status";
     }
 }

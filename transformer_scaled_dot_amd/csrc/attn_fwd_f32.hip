@@ -19,10 +19,10 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
     __shared__ float vs[BNF][D];
 
     const int tid = threadIdx.x;
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks);
-    const int bh = blk / p.n_qtiles;
-    int qt = blk - bh * p.n_qtiles;
-    if (p.causal) qt = p.n_qtiles - 1 - qt;
+    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks));
+    const int bh = bw.bh;
+    int qt = bw.qt;
+    if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;
     const int b = bh / p.H;
     const int q0 = qt * BMF;
     const int qi = q0 + tid;
@@ -39,10 +39,12 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
 
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
     const int q_last = min(p.Nq, q0 + BMF) - 1;
-    int kv_end = kv_valid;
-    if (p.causal) kv_end = min(kv_end, q_last + 1);
-    if (p.window >= 0) kv_end = min(kv_end, q_last + p.window + 1);
-    const int kv_begin = p.window >= 0 ? max(0, q0 - p.window) / BNF * BNF : 0;
+    int kv_end = min(kv_valid, attn::row_key_hi(p, q_last, kv_valid));
+    int kv_begin = max(0, attn::row_key_lo(p, q0)) / BNF * BNF;
+    if (p.n_splits > 1) {  // this workgroup's share of the keys (split_len is a multiple of BNF)
+        kv_begin = max(kv_begin, bw.split * p.split_len);
+        kv_end = min(kv_end, (bw.split + 1) * p.split_len);
+    }
     const int lo = attn::row_key_lo(p, qi), hi = attn::row_key_hi(p, qi, kv_valid);
     const float c2 = p.scale_log2;
 
@@ -94,12 +96,14 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
 
     if (qi < p.Nq) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        float* og = (float*)p.o + ((size_t)bh * p.Nq + qi) * D;
+        const size_t row = p.n_splits > 1 ? ((size_t)bw.split * p.B * p.H + bh) * p.Nq + qi
+                                          : (size_t)bh * p.Nq + qi;
+        float* og = (p.n_splits > 1 ? p.o_part : (float*)p.o) + row * D;
+        float* lg = p.n_splits > 1 ? p.lse_part : p.lse;
 #pragma unroll
         for (int d = 0; d < D; d += 4)
             *(float4*)(og + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-        p.lse[(size_t)bh * p.Nq + qi] =
-            l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * attn::kLn2 : -INFINITY;
+        lg[row] = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * attn::kLn2 : -INFINITY;
     }
 }
 

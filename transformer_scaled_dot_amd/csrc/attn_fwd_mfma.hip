@@ -110,10 +110,10 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks);
-    const int bh = blk / p.n_qtiles;
-    int qt = blk - bh * p.n_qtiles;
-    if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
+    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks));
+    const int bh = bw.bh;
+    int qt = bw.qt;
+    if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;  // longest rows first
     const int b = bh / p.H;
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * 32;
@@ -122,11 +122,14 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     // Key tiles [t_begin, n_tiles) hold every key some row of this workgroup may see.
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
     const int q_last = min(p.Nq, q0 + BM) - 1;
-    int kv_end = kv_valid;
-    if (p.causal) kv_end = min(kv_end, q_last + 1);
-    if (p.window >= 0) kv_end = min(kv_end, q_last + p.window + 1);
+    int kv_end = min(kv_valid, attn::row_key_hi(p, q_last, kv_valid));
+    int k_begin = max(0, attn::row_key_lo(p, q0));
+    if (p.n_splits > 1) {  // this workgroup's share of the keys (split_len is a multiple of BN)
+        k_begin = max(k_begin, bw.split * p.split_len);
+        kv_end = min(kv_end, (bw.split + 1) * p.split_len);
+    }
     const int n_tiles = (kv_end + BN - 1) / BN;
-    const int t_begin = p.window >= 0 ? max(0, q0 - p.window) / BN : 0;
+    const int t_begin = k_begin / BN;
 
     const T* qg = (const T*)p.q + (size_t)bh * p.Nq * D;
     const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
@@ -320,7 +323,22 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
 
     // ---- epilogue: O = O / l (rounded to T), LSE = ln 2 * (m + log2 l)
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qi < p.Nq) {
+    if (p.n_splits > 1) {  // fp32 partial result of this split, merged by attn_merge_kernel
+        if (qi < p.Nq) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const size_t row = ((size_t)bw.split * p.B * p.H + bh) * p.Nq + qi;
+            float* og = p.o_part + row * D;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *(float4*)(og + 32 * t + 8 * a + 4 * g) =
+                        make_float4(oacc[t][4 * a + 0] * inv, oacc[t][4 * a + 1] * inv,
+                                    oacc[t][4 * a + 2] * inv, oacc[t][4 * a + 3] * inv);
+            if (g == 0)
+                p.lse_part[row] = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * attn::kLn2 : -INFINITY;
+        }
+    } else if (qi < p.Nq) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         T* og = (T*)p.o + ((size_t)bh * p.Nq + qi) * D;
 #pragma unroll

@@ -15,15 +15,20 @@ Recipe (one stream per tensor, all counter-based so any slice can be regenerated
   z0 = r cos(2 pi u2), z1 = r sin(2 pi u2), in float64.
 * Value = z * sigma (float64) -> float32 (round to nearest even) -> storage dtype
   (float16 by numpy's RNE cast; bfloat16 by RNE on the float32 bit pattern).
-* Key lengths (padded workloads): 64 + (x mod 449), i.e. uniform on [64, 512].
+* Key lengths (padded workloads): lo + (x mod (Nk - lo + 1)), i.e. uniform on [lo, Nk]
+  (lo = 64 unless the workload says otherwise: [64, 512] for the BERT-like batch).
 
 The workloads mirror the shapes the pages measure: a tiny fp32 case, the (2, 100, 512)
 toy split into 8 heads of 64, BERT-base encoder attention at 512 tokens with padding,
-decoder attention at 4K and long-context attention at 16K with 32 heads of 128.
+decoder attention at 4K and long-context attention at 16K with 32 heads of 128, the same
+two with a sliding window, and KV-cache decode steps (one new query per sequence against a
+4K, 16K or ragged 1K-8K cache of the decoder's 32 heads of 128).
 """
 from __future__ import annotations
 
 import hashlib
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
 import numpy as np
@@ -59,11 +64,14 @@ def uniforms(state: int, start: int, count: int) -> np.ndarray:
     return (x >> np.uint64(11)).astype(np.float64) * (1.0 / 9007199254740992.0)
 
 
-def normals(state: int, count: int, chunk: int = 1 << 22) -> np.ndarray:
-    """`count` standard normals (float64) from Box-Muller pairs of the stream."""
+def normals(state: int, count: int, chunk: int = 1 << 20) -> np.ndarray:
+    """`count` standard normals (float64) from Box-Muller pairs of the stream.  Chunks are
+    independent slices of the counter-based stream, filled by a few threads (numpy releases
+    the GIL inside its array loops); the result does not depend on the thread count."""
     out = np.empty(count, dtype=np.float64)
     npairs = (count + 1) // 2
-    for p0 in range(0, npairs, chunk):
+
+    def fill(p0: int) -> None:
         np_ = min(chunk, npairs - p0)
         u = uniforms(state, 2 * p0, 2 * np_)
         u1, u2 = u[0::2], u[1::2]
@@ -75,6 +83,14 @@ def normals(state: int, count: int, chunk: int = 1 << 22) -> np.ndarray:
         lo = 2 * p0
         hi = min(count, lo + 2 * np_)
         out[lo:hi] = z[: hi - lo]
+
+    starts = range(0, npairs, chunk)
+    if len(starts) <= 1:
+        for p0 in starts:
+            fill(p0)
+    else:
+        with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1, len(starts))) as ex:
+            list(ex.map(fill, starts))
     return out
 
 
@@ -121,6 +137,8 @@ class Workload:
     note: str = ""
     scale: float = field(default=None)  # defaults to 1/sqrt(D), rounded to float32
     window: int = field(default=None)   # local band |i - j| <= window, None for none
+    kv_cache: bool = False  # queries are the last Nq positions of each key sequence (decode)
+    len_lo: int = 64        # padded workloads: key lengths uniform on [len_lo, Nk]
 
     @property
     def scale_f32(self) -> np.float32:
@@ -135,11 +153,22 @@ class Workload:
         hi = np.minimum(hi, i + self.window + 1)
         return int(np.maximum(hi - lo, 0).sum())
 
+    def cache_pairs(self) -> int:
+        """(query, key) pairs of a KV-cache step, padding ignored: query i (the (Nk - Nq + i)-th
+        position) sees keys j <= i + Nk - Nq when causal, every key otherwise."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        i = np.arange(self.Nq, dtype=np.int64)
+        return int(np.clip(i + 1 + self.Nk - self.Nq, 0, self.Nk).sum())
+
     def flops(self) -> float:
         """Metric FLOPs: 4*B*H*Nq*Nk*D, halved for causal (QK^T and PV, dense count).  With a
-        local window: 4*B*H*D per (query, key) pair inside the band."""
+        local window: 4*B*H*D per (query, key) pair inside the band.  A KV-cache step counts
+        4*B*H*D per visible (query, key) pair."""
         if self.window is not None:
             return 4.0 * self.B * self.H * self.D * self.band_pairs()
+        if self.kv_cache:
+            return 4.0 * self.B * self.H * self.D * self.cache_pairs()
         f = 4.0 * self.B * self.H * self.Nq * self.Nk * self.D
         return f / 2 if self.causal else f
 
@@ -167,6 +196,14 @@ WORKLOADS = {
         Workload("longctx_window512_causal_bf16_b1h32n16384d128", "bf16", 1, 32, 16384, 16384, 128, True,
                  False, 0.5, 0.5, 7, "long-context causal attention at 16K with a sliding window of 512",
                  window=512),
+        Workload("kvdecode_bf16_b4h32q1k4096d128", "bf16", 4, 32, 1, 4096, 128, True, False, 0.5, 0.5, 8,
+                 "one decode step of the 4K decoder batch: 1 new query per sequence, full 4K cache",
+                 kv_cache=True),
+        Workload("kvdecode_bf16_b1h32q1k16384d128", "bf16", 1, 32, 1, 16384, 128, True, False, 0.5, 0.5, 9,
+                 "one decode step at 16K context: 1 new query against a 16K cache", kv_cache=True),
+        Workload("kvdecode_ragged_bf16_b16h32q1k8192d128", "bf16", 16, 32, 1, 8192, 128, True, True, 0.5,
+                 0.5, 10, "one decode step of a serving batch: 16 caches of lengths U[1024, 8192]",
+                 kv_cache=True, len_lo=1024),
     ]
 }
 
@@ -175,10 +212,13 @@ BENCH_WORKLOAD = "longctx_causal_bf16_b1h32n16384d128"
 PARITY_ORDER = list(WORKLOADS)
 
 
-def make_key_lens(seed: int, B: int) -> np.ndarray:
+def make_key_lens(seed: int, B: int, Nk: int = 512, lo: int = 64) -> np.ndarray:
+    """Valid key lengths uniform on [lo, Nk] (lo <= Nk)."""
+    if not 0 <= lo <= Nk:
+        raise ValueError("need 0 <= lo <= Nk")
     st = stream_state(seed, 3)
     x = splitmix64(st, 0, B)
-    return (np.uint64(64) + x % np.uint64(449)).astype(np.int32)
+    return (np.uint64(lo) + x % np.uint64(Nk - lo + 1)).astype(np.int32)
 
 
 def make_tensor(seed: int, which: int, shape, sigma: float, dtype: str) -> np.ndarray:
@@ -195,7 +235,7 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     q = make_tensor(s, 0, (w.B, w.H, w.Nq, w.D), w.sigma_qk, w.dtype)
     k = make_tensor(s, 1, (w.B, w.H, w.Nk, w.D), w.sigma_qk, w.dtype)
     v = make_tensor(s, 2, (w.B, w.H, w.Nk, w.D), w.sigma_v, w.dtype)
-    kl = make_key_lens(s, w.B) if w.padded else None
+    kl = make_key_lens(s, w.B, w.Nk, w.len_lo) if w.padded else None
     return {"q": q, "k": k, "v": v, "key_lens": kl, "scale": w.scale_f32, "seed": s}
 
 
