@@ -63,8 +63,9 @@ hipError_t launch(const attn::Params& p, int dtype, int D, hipStream_t s) {
 }
 
 // How a decode call spreads the keys over workgroups: enough splits to give the chip about
-// 2048 workgroups, at most 64, each split at least four 64-key tiles long.  A pure function of
-// the sizes, so the workspace query and the call always agree.
+// 1024 workgroups (four per CU; 512 to 2048 measure within a few percent), at most 64, each
+// split at least four 64-key tiles long.  A pure function of the sizes, so the workspace query
+// and the call always agree.
 struct DecodePlan {
     int n_splits;
     int split_len;
@@ -74,7 +75,7 @@ struct DecodePlan {
 DecodePlan decode_plan(int B, int H, int Nq, int Nk, int D, int dtype) {
     const int bm = dtype == ATTN_F32 ? attn_f32_block_m() : attn_mfma_block_m();
     const int64_t base = (int64_t)B * H * (((int64_t)Nq + bm - 1) / bm);
-    int64_t S = (2048 + base - 1) / base;
+    int64_t S = (1024 + base - 1) / base;
     S = S < 64 ? S : 64;
     const int64_t by_len = Nk / 256;
     S = S < by_len ? S : by_len;

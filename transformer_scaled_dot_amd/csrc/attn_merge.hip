@@ -12,39 +12,61 @@
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int NT = 256;  // threads per row
 
+// One workgroup per query row.  Wave 0 turns the splits' LSEs (one per lane, S <= 64) into
+// normalised weights w_s = e^{LSE_s - LSE}; then every thread owns one float4 column of O and
+// every (NT / (D/4))-th split, so all of a row's partial-O loads are in flight at once, and
+// the per-group sums meet in LDS.
 template <typename T, int D>
-__global__ void __launch_bounds__(64) attn_merge_kernel(attn::Params p) {
-    constexpr int PER = D / 64;  // output elements per lane
-    const int lane = threadIdx.x;
+__global__ void __launch_bounds__(NT) attn_merge_kernel(attn::Params p) {
+    constexpr int C4 = D / 4;     // float4 columns per row
+    constexpr int NG = NT / C4;   // split groups
+    __shared__ float wsh[64];
+    __shared__ float4 red[NG][C4];
+
+    const int tid = threadIdx.x;
     const size_t row = blockIdx.x;  // (b * H + h) * Nq + i
     const size_t plane = (size_t)p.B * p.H * p.Nq;
-    const int S = p.n_splits;  // <= 64: one split per lane
+    const int S = p.n_splits;
 
-    const float ls = lane < S ? p.lse_part[lane * plane + row] : -INFINITY;
-    float m = ls;
+    if (tid < 64) {
+        const float ls = tid < S ? p.lse_part[tid * plane + row] : -INFINITY;
+        float m = ls;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    const float w = (lane < S && m != -INFINITY) ? __builtin_amdgcn_exp2f((ls - m) * kLog2e) : 0.f;
-    float l = w;
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        const float e = (tid < S && m != -INFINITY) ? __builtin_amdgcn_exp2f((ls - m) * kLog2e) : 0.f;
+        float l = e;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float ws = __shfl(w, s);
-        if (ws == 0.f) continue;  // the same on every lane
-        const float* op = p.o_part + (s * plane + row) * D;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = __builtin_fmaf(ws, op[lane + 64 * e], acc[e]);
+        for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+        wsh[tid] = l > 0.f ? e / l : 0.f;
+        if (tid == 0) p.lse[row] = l > 0.f ? m + __builtin_amdgcn_logf(l) * attn::kLn2 : -INFINITY;
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* og = (T*)p.o + row * D;
+    __syncthreads();
+
+    const int g = tid / C4, c = tid - g * C4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) og[lane + 64 * e] = (T)(acc[e] * inv);
-    if (lane == 0) p.lse[row] = l > 0.f ? m + __builtin_amdgcn_logf(l) * attn::kLn2 : -INFINITY;
+    for (int k = 0; k < 64 / NG; ++k) {
+        const int sp = g + k * NG;
+        if (sp < S) {
+            const float w = wsh[sp];
+            const float4 v = *((const float4*)(p.o_part + (sp * plane + row) * D) + c);
+            acc.x = __builtin_fmaf(w, v.x, acc.x);
+            acc.y = __builtin_fmaf(w, v.y, acc.y);
+            acc.z = __builtin_fmaf(w, v.z, acc.z);
+            acc.w = __builtin_fmaf(w, v.w, acc.w);
+        }
+    }
+    red[g][c] = acc;
+    __syncthreads();
+    if (tid < D) {
+        const float* rf = (const float*)&red[0][0];
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) o += rf[k * D + tid];
+        ((T*)p.o)[row * D + tid] = (T)o;
+    }
 }
 
 template <typename T, int D>
@@ -52,7 +74,7 @@ hipError_t launch_one(const attn::Params& p, hipStream_t stream) {
     attn::Params pc = p;
     void* args[] = {&pc};
     return hipLaunchKernel((const void*)attn_merge_kernel<T, D>,
-                           dim3((unsigned)((size_t)p.B * p.H * p.Nq)), dim3(64), args, 0, stream);
+                           dim3((unsigned)((size_t)p.B * p.H * p.Nq)), dim3(NT), args, 0, stream);
 }
 
 }  // namespace
