@@ -44,6 +44,13 @@ class Oracle:
             ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.oracle_decode.restype = ctypes.c_double
         lib.oracle_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -100,6 +107,46 @@ class Oracle:
         o, lse = self.attn_rows(q, k, v, dtype, scale, causal, key_lens, None, nthreads, window)
         return o.reshape(B, H, Nq, D), lse.reshape(B, H, Nq)
 
+    def attn_bwd(self, q, k, v, do, dtype: str, scale, causal: bool = False, key_lens=None,
+                 dlse=None, bh=None, nthreads: int = 0):
+        """Reference gradients dQ, dK, dV (fp64) of the attention forward.
+
+        q, do: [B,H,Nq,D]; k, v: [B,H,Nk,D] in storage form (bf16 as uint16 bits); do is the
+        gradient of the loss with respect to O.  dlse: float32 [B,H,Nq] gradient with respect
+        to the LSE output, or None (zero).  causal: False/True (top-left).  bh: slice ids
+        b*H + h to compute, or None for all.  Returns dq [n,Nq,D], dk [n,Nk,D], dv [n,Nk,D]
+        for the n selected slices, reshaped to [B,H,...] when bh is None.
+        """
+        q = _as_storage(q, dtype)
+        k = _as_storage(k, dtype)
+        v = _as_storage(v, dtype)
+        do = _as_storage(do, dtype)
+        B, H, Nq, D = q.shape
+        Nk = k.shape[2]
+        if k.shape != (B, H, Nk, D) or v.shape != (B, H, Nk, D) or do.shape != q.shape:
+            raise ValueError("k, v must be [B,H,Nk,D] and do like q")
+        if int(causal) not in (0, 1):
+            raise ValueError("causal must be 0 or 1")
+        kl = None if key_lens is None else np.ascontiguousarray(key_lens, dtype=np.int32)
+        if kl is not None and kl.shape != (B,):
+            raise ValueError("key_lens must be int32[B]")
+        g = None if dlse is None else np.ascontiguousarray(dlse, dtype=np.float32)
+        if g is not None and g.shape != (B, H, Nq):
+            raise ValueError("dlse must be float32[B,H,Nq]")
+        sel = None if bh is None else np.ascontiguousarray(bh, dtype=np.int64).reshape(-1)
+        n = B * H if sel is None else sel.size
+        dq = np.empty((n, Nq, D), np.float64)
+        dk = np.empty((n, Nk, D), np.float64)
+        dv = np.empty((n, Nk, D), np.float64)
+        rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(g), _CODES[dtype],
+                                      B, H, Nq, Nk, D, float(scale), int(causal), _ptr(kl),
+                                      _ptr(sel), n, _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_bwd failed with {rc}")
+        if sel is None:
+            return dq.reshape(B, H, Nq, D), dk.reshape(B, H, Nk, D), dv.reshape(B, H, Nk, D)
+        return dq, dk, dv
+
     def decode(self, a: np.ndarray, dtype: str) -> np.ndarray:
         """The oracle's own widening of stored values to fp64 (element by element)."""
         a = _as_storage(a, dtype)
@@ -140,6 +187,10 @@ def attn_rows(*a, **kw):
 
 def attn(*a, **kw):
     return default().attn(*a, **kw)
+
+
+def attn_bwd(*a, **kw):
+    return default().attn_bwd(*a, **kw)
 
 
 def decode(a, dtype):

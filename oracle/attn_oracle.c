@@ -2,8 +2,9 @@
  * attn_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow, obviously correct fp64 CPU reference for the forward pass of
- * multi-head scaled-dot-product attention.  Only the test suite, the smoke check and
- * the benchmark's CPU-baseline leg may load this library; the product path never does.
+ * multi-head scaled-dot-product attention and for its gradients (oracle_attn_bwd, below).
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may load this
+ * library; the product path never does.
  * It shares no code, header or constant with the HIP library.
  *
  * What it computes (the textbook definition, not the tiled algorithm):
@@ -204,6 +205,178 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int
                      const int64_t* rows, int64_t nrows, double* o, double* lse, int nthreads) {
     return oracle_attn_rows_window(q, k, v, dtype, B, H, Nq, Nk, D, scale, causal, -1, key_lens,
                                    rows, nrows, o, lse, nthreads);
+}
+
+/*
+ * Backward pass (gradients of the forward above, for causal in {0, 1} and no window).
+ *
+ * With the row probabilities P[i,j] = e_j / l over J(i) (0 outside it) and a scalar loss whose
+ * gradients with respect to the outputs are dO (same shape as O) and dlse (same shape as lse,
+ * zero when not given), the chain rule through O[i,:] = sum_j P[i,j] v[j,:] and
+ * lse[i] = ln sum_{j in J(i)} exp(s[i,j]) gives
+ *   dv[j,:]  = sum_i P[i,j] dO[i,:]
+ *   dP[i,j]  = dO[i,:] . v[j,:]
+ *   Dr[i]    = sum_j P[i,j] dP[i,j]
+ *   dS[i,j]  = P[i,j] (dP[i,j] - Dr[i] + dlse[i])      (the softmax Jacobian, plus d lse / d s = P)
+ *   dq[i,:]  = scale sum_j dS[i,j] k[j,:]
+ *   dk[j,:]  = scale sum_i dS[i,j] q[i,:]
+ * Source: the pages say training must keep or rebuild the softmax output for the backward pass
+ * (aicoding.csdn.net ch.1 list) and that FlashAttention-2's backward rebuilds the products from
+ * the forward's softmax instead of storing the N x N matrix (hotelren.com sec.4.2, "gradient
+ * back-propagation reconstruction"; its printed helper is garbled, so the gradient itself is
+ * taken from the calculus above).
+ *
+ * Pass 1 (over query rows): P from the definition (two-pass max), Dr[i], lse[i] and dq[i,:].
+ * Pass 2 (over keys): P[i,j] = exp(s[i,j] - lse[i]) for every row i that sees key j, then dk and
+ * dv.  Both passes are plain sums in fp64; the second re-derives P from lse only so that each
+ * key's sums can be formed independently.
+ */
+typedef struct {
+    int dtype, Nq, Nk, D, causal;
+    double scale;
+} bwd_shape;
+
+/* keys [0, jend) visible to row i of a batch with L valid keys (causal 0 / 1) */
+static int64_t bwd_jend(const bwd_shape* sh, int64_t L, int i) {
+    int64_t jend = L;
+    if (sh->causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;
+    return jend;
+}
+
+/*
+ * oracle_attn_bwd -- reference gradients for selected (b, h) slices.
+ *   q, dO: [B,H,Nq,D]; k, v: [B,H,Nk,D]; contiguous, stored as `dtype`.
+ *   dlse: fp32 [B,H,Nq] or NULL (zero).  causal: 0 or 1.  key_lens: int32[B] or NULL.
+ *   bh: slice ids b*H + h (n_bh of them), or NULL for all B*H in order.
+ *   dq: fp64 [n_bh, Nq, D]; dk, dv: fp64 [n_bh, Nk, D].
+ * Returns 0, -1 on a bad argument, -2 if memory cannot be allocated.
+ */
+int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
+                    const float* dlse, int dtype, int B, int H, int Nq, int Nk, int D,
+                    double scale, int causal, const int32_t* key_lens, const int64_t* bh,
+                    int64_t n_bh, double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dO || !dq || !dk || !dv) return -1;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return -1;
+    if (causal != 0 && causal != 1) return -1;
+    if (!bh) n_bh = (int64_t)B * H;
+    for (int64_t t = 0; bh && t < n_bh; ++t)
+        if (bh[t] < 0 || bh[t] >= (int64_t)B * H) return -1;
+    int nt = 1;
+#ifdef _OPENMP
+    nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#endif
+    (void)nthreads;
+    const bwd_shape sh = {dtype, Nq, Nk, D, causal, scale};
+    /* one slice at a time: its inputs widened to fp64, lse and Dr per row */
+    const size_t nq = (size_t)Nq * D, nk = (size_t)Nk * D;
+    double* buf = (double*)malloc(sizeof(double) * (2 * nq + 2 * nk + 2 * (size_t)Nq));
+    const size_t per = 2 * (size_t)Nk; /* per thread: P[Nk], dP[Nk] of one row */
+    double* sc = (double*)malloc(sizeof(double) * (size_t)nt * per);
+    if (!buf || !sc) {
+        free(buf);
+        free(sc);
+        return -2;
+    }
+    double *Qd = buf, *dOd = Qd + nq, *Kd = dOd + nq, *Vd = Kd + nk, *lse = Vd + nk, *Dr = lse + Nq;
+    for (int64_t t = 0; t < n_bh; ++t) {
+        const int64_t s_bh = bh ? bh[t] : t;
+        const int b = (int)(s_bh / H);
+        int64_t L = Nk;
+        if (key_lens) {
+            L = key_lens[b];
+            if (L < 0) L = 0;
+            if (L > Nk) L = Nk;
+        }
+        for (size_t x = 0; x < nq; ++x) {
+            Qd[x] = dec(q, dtype, (int64_t)(s_bh * nq + x));
+            dOd[x] = dec(dO, dtype, (int64_t)(s_bh * nq + x));
+        }
+        for (size_t x = 0; x < nk; ++x) {
+            Kd[x] = dec(k, dtype, (int64_t)(s_bh * nk + x));
+            Vd[x] = dec(v, dtype, (int64_t)(s_bh * nk + x));
+        }
+        double* dqs = dq + t * nq;
+        double* dks = dk + t * nk;
+        double* dvs = dv + t * nk;
+
+        /* pass 1: rows */
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 8)
+        for (int i = 0; i < Nq; ++i) {
+            int tid = 0;
+#ifdef _OPENMP
+            tid = omp_get_thread_num();
+#endif
+            double* P = sc + (size_t)tid * per;
+            double* dP = P + Nk;
+            const double* qi = Qd + (size_t)i * D;
+            const double* gi = dOd + (size_t)i * D;
+            double* dqi = dqs + (size_t)i * D;
+            for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+            const int64_t n = bwd_jend(&sh, L, i);
+            if (n <= 0) {
+                lse[i] = -INFINITY;
+                Dr[i] = 0.0;
+                continue;
+            }
+            /* logits, max, sum, probabilities */
+            double m = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += qi[d] * Kd[j * D + d];
+                P[j] = sh.scale * acc;
+                if (P[j] > m) m = P[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < n; ++j) l += exp(P[j] - m);
+            lse[i] = m + log(l);
+            for (int64_t j = 0; j < n; ++j) P[j] = exp(P[j] - m) / l;
+            /* dP and Dr = sum_j P dP */
+            double Dsum = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += gi[d] * Vd[j * D + d];
+                dP[j] = acc;
+                Dsum += P[j] * acc;
+            }
+            Dr[i] = Dsum;
+            /* dq = scale sum_j P (dP - Dr + g) k_j */
+            const double g = dlse ? (double)dlse[s_bh * Nq + i] : 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                const double ds = P[j] * (dP[j] - Dsum + g);
+                for (int d = 0; d < D; ++d) dqi[d] += sh.scale * ds * Kd[j * D + d];
+            }
+        }
+
+        /* pass 2: keys */
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 8)
+        for (int j = 0; j < Nk; ++j) {
+            double* dkj = dks + (size_t)j * D;
+            double* dvj = dvs + (size_t)j * D;
+            for (int d = 0; d < D; ++d) dkj[d] = dvj[d] = 0.0;
+            if (j >= L) continue; /* padding keys are never seen */
+            for (int i = 0; i < Nq; ++i) {
+                if ((int64_t)j >= bwd_jend(&sh, L, i)) continue;
+                const double* qi = Qd + (size_t)i * D;
+                const double* gi = dOd + (size_t)i * D;
+                double acc = 0.0, dp = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    acc += qi[d] * Kd[(size_t)j * D + d];
+                    dp += gi[d] * Vd[(size_t)j * D + d];
+                }
+                const double pij = exp(sh.scale * acc - lse[i]);
+                const double g = dlse ? (double)dlse[s_bh * Nq + i] : 0.0;
+                const double ds = pij * (dp - Dr[i] + g);
+                for (int d = 0; d < D; ++d) {
+                    dkj[d] += sh.scale * ds * qi[d];
+                    dvj[d] += pij * gi[d];
+                }
+            }
+        }
+    }
+    free(buf);
+    free(sc);
+    return 0;
 }
 
 /* Decoders exposed for the tests' checks of the widening itself. */

@@ -20,7 +20,10 @@ What the pins rest on (none of them re-types the oracle's formula):
   * a library special case: torch's scaled_dot_product_attention in float64 with a boolean
     mask (True = may attend);
   * brute force at 50 digits (oracle/bruteforce.py) and the golden fixture it wrote;
-  * the storage decoders against numpy / torch widening of every 16-bit pattern.
+  * the storage decoders against numpy / torch widening of every 16-bit pattern;
+  * for the gradients: central differences of the forward oracle's own loss, torch autograd in
+    float64, closed forms (one key, uniform weights, an LSE gradient alone) and invariants (the
+    sums of dV and dK over keys, row and key permutations).
 """
 from __future__ import annotations
 
@@ -496,10 +499,205 @@ def pin_decoders(impl):
     assert np.array_equal(impl.decode(f, "f32"), f.astype(np.float64)), "fp32 decode"
 
 
+# ---------------------------------------------------------------- backward (gradients)
+def visible(i, L, causal):
+    """Keys row i may attend to (top-left causal), written out from the mask's definition."""
+    return [j for j in range(L) if not causal or j <= i]
+
+
+def pin_bwd_finite_differences(impl):
+    """Directional central differences of the forward oracle's loss
+    L = sum(O * G) + sum(lse * g) along random perturbations of Q, K and V (fp32 storage; the
+    step actually taken is the difference of the two stored points) equal the backward's
+    gradients dotted with the step."""
+    rng = np.random.default_rng(31)
+    for causal in (False, True):
+        for with_g in (False, True):
+            B, H, Nq, Nk, D = 2, 2, 6, 9, 5
+            scale = 0.4
+            x = {n: rand_store(rng, (B, H, Nq if n == "q" else Nk, D), "f32") for n in "qkv"}
+            G = rand_store(rng, (B, H, Nq, D), "f32")
+            g = rng.standard_normal((B, H, Nq)).astype(np.float32) if with_g else None
+            kl = np.array([9, 4], np.int32)
+            dq, dk, dv = impl.attn_bwd(x["q"], x["k"], x["v"], G, "f32", scale, causal, kl, g)
+            grads = {"q": dq, "k": dk, "v": dv}
+
+            def loss(xx):
+                o, lse = impl.attn(xx["q"], xx["k"], xx["v"], "f32", scale, causal, kl)
+                fin = np.isfinite(lse)
+                val = float(np.sum(o * G.astype(np.float64)))
+                if g is not None:
+                    val += float(np.sum((lse * g.astype(np.float64))[fin]))
+                return val
+
+            for name in "qkv":
+                for _ in range(3):
+                    u = rng.standard_normal(x[name].shape) * 1e-3
+                    xp, xm = dict(x), dict(x)
+                    xp[name] = (x[name].astype(np.float64) + u).astype(np.float32)
+                    xm[name] = (x[name].astype(np.float64) - u).astype(np.float32)
+                    step = xp[name].astype(np.float64) - xm[name].astype(np.float64)
+                    fd = loss(xp) - loss(xm)
+                    an = float(np.sum(grads[name] * step))
+                    assert abs(fd - an) <= 1e-5 * max(abs(fd), 1e-3), \
+                        f"d/d{name} causal={causal} dlse={with_g}: fd {fd:.9e} vs {an:.9e}"
+
+
+def torch_grads_f64(q, k, v, do, dtype, scale, causal, key_lens, dlse=None):
+    """Gradients of sum(O * dO) + sum(lse * dlse) by torch autograd in float64 through the
+    explicit masked softmax (True = may attend); rows with no valid key contribute nothing."""
+    import torch
+
+    qd, kd, vd = (torch.tensor(storage_to_f64(t, dtype), requires_grad=True) for t in (q, k, v))
+    G = torch.from_numpy(storage_to_f64(do, dtype))
+    B, H, Nq, _ = qd.shape
+    Nk = kd.shape[2]
+    i = torch.arange(Nq)[:, None]
+    j = torch.arange(Nk)[None, :]
+    allow = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
+    if causal:
+        allow &= (j <= i)[None, None]
+    if key_lens is not None:
+        allow &= (j[None] < torch.from_numpy(np.asarray(key_lens, np.int64))[:, None, None])[:, None]
+    s = torch.matmul(qd, kd.transpose(-2, -1)) * float(scale)
+    s = s.masked_fill(~allow, float("-inf"))
+    live = allow.any(-1, keepdim=True)
+    s = torch.where(live, s, torch.zeros_like(s))  # empty rows: no -inf - -inf
+    p = torch.softmax(s, dim=-1) * live
+    o = torch.matmul(p, vd)
+    loss = (o * G).sum()
+    if dlse is not None:
+        lse = torch.logsumexp(s, dim=-1)
+        loss = loss + (lse * torch.from_numpy(np.asarray(dlse, np.float64)) * live[..., 0]).sum()
+    loss.backward()
+    return qd.grad.numpy(), kd.grad.numpy(), vd.grad.numpy()
+
+
+def pin_bwd_torch_autograd(impl):
+    """Library special case: torch autograd in float64, three dtypes, every mask combination,
+    an empty row, with and without an LSE gradient."""
+    rng = np.random.default_rng(32)
+    for dtype in ("f32", "f16", "bf16"):
+        for causal in (False, True):
+            for padded in (False, True):
+                for with_g in (False, True):
+                    B, H, Nq, Nk, D = 3, 2, 7, 10, 8
+                    q, do = (rand_store(rng, (B, H, Nq, D), dtype) for _ in range(2))
+                    k, v = (rand_store(rng, (B, H, Nk, D), dtype) for _ in range(2))
+                    kl = np.array([10, 5, 0], np.int32) if padded else None
+                    g = rng.standard_normal((B, H, Nq)).astype(np.float32) if with_g else None
+                    scale = float(np.float32(1 / math.sqrt(D)))
+                    got = impl.attn_bwd(q, k, v, do, dtype, scale, causal, kl, g)
+                    want = torch_grads_f64(q, k, v, do, dtype, scale, causal, kl, g)
+                    for n, a, b in zip(("dq", "dk", "dv"), got, want):
+                        close(a, b, 1e-12, f"autograd {n} {dtype} causal={causal} padded={padded} dlse={with_g}")
+
+
+def pin_bwd_closed_forms(impl):
+    """One key: dq = 0, dk = scale * sum_i g_i q_i, dv = sum of dO over the rows.  Q = 0 (and
+    scale = 0): uniform weights, dv_j = sum over rows seeing j of dO_i / |J(i)|, dk = 0.
+    dO = 0 with an LSE gradient: dq_i = scale * g_i * (attention of q_i over K with V = K),
+    dv = 0.  Keys no row sees get exactly zero gradients; empty rows get dq = 0."""
+    rng = np.random.default_rng(33)
+    # one key
+    for dtype in ("f32", "bf16"):
+        B, H, Nq, D = 2, 2, 5, 8
+        q, do = (rand_store(rng, (B, H, Nq, D), dtype) for _ in range(2))
+        k, v = (rand_store(rng, (B, H, 1, D), dtype) for _ in range(2))
+        g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+        dq, dk, dv = impl.attn_bwd(q, k, v, do, dtype, 0.3, False, None, None)
+        assert np.all(dq == 0), "one key: dq = 0"
+        assert np.all(dk == 0), "one key, no dlse: dk = 0"
+        close(dv[:, :, 0], storage_to_f64(do, dtype).sum(axis=2), 1e-13, "one key: dv = sum dO")
+        dq, dk, dv = impl.attn_bwd(q, k, v, do, dtype, 0.3, False, None, g)
+        qd = storage_to_f64(q, dtype)
+        close(dk[:, :, 0], 0.3 * np.einsum("bhi,bhid->bhd", g.astype(np.float64), qd), 1e-13,
+              "one key: dk = scale sum g q")
+        close(dq, 0.3 * g.astype(np.float64)[..., None] * storage_to_f64(k, dtype), 1e-13,
+              "one key: dq = scale g k")
+    # Q = 0 and scale = 0
+    for dtype in ("f32", "bf16"):
+        for causal in (False, True):
+            B, H, Nq, Nk, D = 2, 2, 6, 8, 4
+            k, v = (rand_store(rng, (B, H, Nk, D), dtype) for _ in range(2))
+            q = rand_store(rng, (B, H, Nq, D), dtype)
+            do = rand_store(rng, (B, H, Nq, D), dtype)
+            kl = np.array([8, 3], np.int32)
+            dod = storage_to_f64(do, dtype)
+            for qq, sc in ((store(np.zeros((B, H, Nq, D)), dtype), 0.5), (q, 0.0)):
+                dq, dk, dv = impl.attn_bwd(qq, k, v, do, dtype, sc, causal, kl)
+                want = np.zeros((B, H, Nk, D))
+                for b in range(B):
+                    for i in range(Nq):
+                        J = visible(i, int(kl[b]), causal)
+                        for j in J:
+                            want[b, :, j] += dod[b, :, i] / len(J)
+                close(dv, want, 1e-14, f"uniform weights: dv {dtype} causal={causal} scale={sc}")
+                assert np.all(dk == 0), "uniform weights: dk = 0"
+                if sc == 0.0:
+                    assert np.all(dq == 0), "scale 0: dq = 0"
+    # dO = 0, LSE gradient only
+    for causal in (False, True):
+        B, H, Nq, Nk, D = 2, 2, 6, 7, 8
+        q = rand_store(rng, (B, H, Nq, D), "f32")
+        k, v = (rand_store(rng, (B, H, Nk, D), "f32") for _ in range(2))
+        g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+        kl = np.array([7, 4], np.int32)
+        dq, dk, dv = impl.attn_bwd(q, k, v, store(np.zeros((B, H, Nq, D)), "f32"), "f32", 0.7,
+                                   causal, kl, g)
+        ok, _ = impl.attn(q, k, k, "f32", 0.7, causal, kl)  # attention with V = K
+        close(dq, 0.7 * g.astype(np.float64)[..., None] * ok, 1e-13, "dlse only: dq")
+        assert np.all(dv == 0), "dlse only: dv = 0"
+    # keys nobody sees, empty rows
+    B, H, Nq, Nk, D = 2, 1, 4, 9, 4
+    q, do = (rand_store(rng, (B, H, Nq, D), "f32") for _ in range(2))
+    k, v = (rand_store(rng, (B, H, Nk, D), "f32") for _ in range(2))
+    kl = np.array([7, 0], np.int32)
+    dq, dk, dv = impl.attn_bwd(q, k, v, do, "f32", 0.5, True, kl)
+    assert np.all(dk[0, :, Nq:] == 0) and np.all(dv[0, :, Nq:] == 0), "causal: keys past the last row"
+    assert np.all(dk[1] == 0) and np.all(dv[1] == 0) and np.all(dq[1] == 0), "empty batch"
+
+
+def pin_bwd_invariants(impl):
+    """sum_j dv_j = sum of dO over rows that keep a key (each row's weights sum to one);
+    sum_j dk_j = scale * sum_i g_i q_i (each row's dS sums to its LSE gradient); permuting the
+    query rows (with dO and the LSE gradient) permutes dq and leaves dk, dv unchanged; permuting
+    keys with their values permutes dk and dv and leaves dq unchanged (non-causal)."""
+    rng = np.random.default_rng(34)
+    B, H, Nq, Nk, D = 2, 2, 9, 11, 6
+    for causal in (False, True):
+        q, do = (rand_store(rng, (B, H, Nq, D), "f32") for _ in range(2))
+        k, v = (rand_store(rng, (B, H, Nk, D), "f32") for _ in range(2))
+        g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+        kl = np.array([11, 5], np.int32)
+        dq, dk, dv = impl.attn_bwd(q, k, v, do, "f32", 0.45, causal, kl, g)
+        live = np.array([[len(visible(i, int(kl[b]), causal)) > 0 for i in range(Nq)] for b in range(B)])
+        dod, qd = do.astype(np.float64), q.astype(np.float64)
+        close(dv.sum(axis=2), (dod * live[:, None, :, None]).sum(axis=2), 1e-13, "sum dv")
+        gq = 0.45 * g.astype(np.float64)[..., None] * qd * live[:, None, :, None]
+        close(dk.sum(axis=2), gq.sum(axis=2), 1e-13, "sum dk")
+    q, do = (rand_store(rng, (B, H, Nq, D), "f32") for _ in range(2))
+    k, v = (rand_store(rng, (B, H, Nk, D), "f32") for _ in range(2))
+    g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+    dq, dk, dv = impl.attn_bwd(q, k, v, do, "f32", 0.45, False, None, g)
+    pq, pk = rng.permutation(Nq), rng.permutation(Nk)
+    rq = impl.attn_bwd(np.ascontiguousarray(q[:, :, pq]), k, v, np.ascontiguousarray(do[:, :, pq]),
+                       "f32", 0.45, False, None, np.ascontiguousarray(g[:, :, pq]))
+    close(rq[0], dq[:, :, pq], 1e-13, "row permutation: dq")
+    close(rq[1], dk, 1e-13, "row permutation: dk")
+    close(rq[2], dv, 1e-13, "row permutation: dv")
+    rk = impl.attn_bwd(q, np.ascontiguousarray(k[:, :, pk]), np.ascontiguousarray(v[:, :, pk]), do,
+                       "f32", 0.45, False, None, g)
+    close(rk[0], dq, 1e-13, "key permutation: dq")
+    close(rk[1], dk[:, :, pk], 1e-13, "key permutation: dk")
+    close(rk[2], dv[:, :, pk], 1e-13, "key permutation: dv")
+
+
 ALL_PINS = [
     pin_zero_query_mean, pin_scale_zero, pin_causal_row0, pin_single_key, pin_two_keys,
     pin_one_hot_dominant, pin_huge_logit_gap, pin_empty_rows, pin_rows_sum_to_one,
     pin_permutations, pin_key_shift, pin_chunked_lse, pin_torch_sdpa_small,
     pin_torch_sdpa_window, pin_window_zero_query_mean, pin_window_extremes, pin_bottom_right_causal,
     pin_golden_bruteforce, pin_decoders,
+    pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_closed_forms, pin_bwd_invariants,
 ]

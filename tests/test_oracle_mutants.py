@@ -20,8 +20,8 @@ MUTANTS = [
     ("LSE without the max", "*lse = m + log(l);", "*lse = log(l);"),
     ("causal j < i", "jend = (int64_t)i + cb + 1;", "jend = (int64_t)i + cb;"),
     ("causal ignored", "if (causal && jend > (int64_t)i + cb + 1)", "if (0 && jend > (int64_t)i + cb + 1)"),
-    ("key lengths ignored", "L = key_lens[b];", "L = Nk;"),
-    ("key length off by one", "L = key_lens[b];", "L = key_lens[b] - 1;"),
+    ("key lengths ignored", "\n        L = key_lens[b];", "\n        L = Nk;"),
+    ("key length off by one", "\n        L = key_lens[b];", "\n        L = key_lens[b] - 1;"),
     ("batch index from head", "int b = (int)(bh / H);", "int b = (int)(bh % H);"),
     ("K/V base uses Nq", "int64_t kbase = bh * (int64_t)Nk * D;", "int64_t kbase = bh * (int64_t)Nq * D;"),
     ("V rows reversed", "decode_row(v, dtype, kbase + (jbeg + j) * D, D, krow);",
@@ -43,6 +43,25 @@ MUTANTS = [
     ("fp16 bias off by one", "e - 25);", "e - 24);"),
     ("fp16 subnormal scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
     ("sum of unshifted exps", "l += s[j];", "l += s[j] * exp(m);"),
+    # backward
+    ("bwd dq without scale", "dqi[d] += sh.scale * ds * Kd[j * D + d];", "dqi[d] += ds * Kd[j * D + d];"),
+    ("bwd dq from V", "dqi[d] += sh.scale * ds * Kd[j * D + d];", "dqi[d] += sh.scale * ds * Vd[j * D + d];"),
+    ("bwd dk without scale", "dkj[d] += sh.scale * ds * qi[d];", "dkj[d] += ds * qi[d];"),
+    ("bwd dk from dO", "dkj[d] += sh.scale * ds * qi[d];", "dkj[d] += sh.scale * ds * gi[d];"),
+    ("bwd dv weighted by dS", "dvj[d] += pij * gi[d];", "dvj[d] += ds * gi[d];"),
+    ("bwd row term dropped (dq)", "const double ds = P[j] * (dP[j] - Dsum + g);", "const double ds = P[j] * (dP[j] + g);"),
+    ("bwd row term dropped (dk)", "const double ds = pij * (dp - Dr[i] + g);", "const double ds = pij * (dp + g);"),
+    ("bwd LSE gradient sign", "const double ds = P[j] * (dP[j] - Dsum + g);", "const double ds = P[j] * (dP[j] - Dsum - g);"),
+    ("bwd LSE gradient ignored (dk)", "const double ds = pij * (dp - Dr[i] + g);", "const double ds = pij * (dp - Dr[i]);"),
+    ("bwd row term without P", "Dsum += P[j] * acc;", "Dsum += acc;"),
+    ("bwd P not normalised", "P[j] = exp(P[j] - m) / l;", "P[j] = exp(P[j] - m);"),
+    ("bwd lse without max", "lse[i] = m + log(l);", "lse[i] = log(l);"),
+    ("bwd causal ignored in key pass", "if ((int64_t)j >= bwd_jend(&sh, L, i)) continue;", ""),
+    ("bwd causal off by one", "if (sh->causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;",
+     "if (sh->causal && jend > (int64_t)i) jend = (int64_t)i;"),
+    ("bwd dO decoded from Q", "dOd[x] = dec(dO, dtype, (int64_t)(s_bh * nq + x));", "dOd[x] = dec(q, dtype, (int64_t)(s_bh * nq + x));"),
+    ("bwd key lengths ignored", "            L = key_lens[b];\n            if (L < 0) L = 0;\n            if (L > Nk) L = Nk;\n        }\n        for (size_t x",
+     "            L = Nk;\n        }\n        for (size_t x"),
 ]
 
 
