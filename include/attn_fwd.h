@@ -45,13 +45,13 @@ typedef enum {
     ATTN_ERR_NULL = -1,     /* q, k, v, o or lse is NULL */
     ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, or a size beyond the 32-bit limits below */
     ATTN_ERR_HEAD_DIM = -3, /* D is not 64 or 128 */
-    ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype */
+    ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype (attn_bwd: not ATTN_F16 / ATTN_BF16) */
     ATTN_ERR_SCALE = -5,    /* scale is not finite */
     ATTN_ERR_FLAG = -6,     /* causal is not 0 or 1 */
     ATTN_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
     ATTN_ERR_ALIGN = -8,    /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
     ATTN_ERR_WINDOW = -9,   /* window is below -1 (attn_fwd_window) */
-    ATTN_ERR_WORKSPACE = -10 /* workspace smaller than attn_decode_workspace_size() (attn_decode) */
+    ATTN_ERR_WORKSPACE = -10 /* workspace smaller than the *_workspace_size() query (attn_decode, attn_bwd) */
 } attn_status;
 
 /*

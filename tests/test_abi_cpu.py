@@ -136,3 +136,34 @@ def test_decode_workspace_size():
     for bad in ((0, 1, 1, 4096, 64, 2), (1, 1, 1, 4096, 80, 2), (1, 1, 1, 4096, 64, 7),
                 (1, 1, 0, 4096, 64, 2)):
         assert ws(*bad) == 0
+
+
+BWD_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dlse=None, dq=FAKE, dk=FAKE, dv=FAKE,
+              B=2, H=3, Nq=40, Nk=50, D=128, scale=0.088, causal=1, key_lens=None, dtype=2,
+              ws=FAKE, ws_bytes=1 << 20, stream=None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(do=None), -1), (dict(dv=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(Nk=0), -2), (dict(D=96), -3), (dict(dtype=0), -4), (dict(dtype=3), -4),
+    (dict(scale=float("nan")), -5), (dict(causal=2), -6), (dict(dq=FAKE + 4), -8),
+    (dict(dlse=FAKE + 4), -8), (dict(key_lens=FAKE + 1), -8), (dict(ws=None), -1),
+    (dict(ws=FAKE + 8), -8), (dict(ws_bytes=2 * 2 * 3 * 64 * 4 - 1), -10), (dict(Nq=1 << 22, D=128), -2),
+])
+def test_host_validation_bwd(over, code):
+    """attn_bwd checks every argument on the host before anything is enqueued."""
+    a = dict(BWD_OK)
+    a.update(over)
+    rc = binding.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dlse"], a["dq"], a["dk"],
+                          a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"], a["causal"],
+                          a["key_lens"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code
+
+
+def test_bwd_workspace_size():
+    """Two fp32 planes of [B, H, Nq rounded up to 32]; 0 for an empty shape."""
+    ws = binding.attn_bwd_workspace_size
+    assert ws(2, 3, 40) == 2 * 2 * 3 * 64 * 4
+    assert ws(1, 1, 32) == 2 * 32 * 4
+    assert ws(1, 32, 16384) == 2 * 32 * 16384 * 4
+    assert ws(0, 1, 1) == 0 and ws(1, 0, 1) == 0 and ws(1, 1, 0) == 0

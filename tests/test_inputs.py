@@ -125,3 +125,12 @@ def test_key_length_range():
     assert kl.shape == (16,) and kl.min() >= 1024 and kl.max() <= 8192
     with pytest.raises(ValueError):
         inputs.make_key_lens(1, 4, 10, 11)
+
+
+def test_grad_out_stream():
+    """dO has a stream of its own (4): N(0, 1), deterministic, different from Q."""
+    w = inputs.Workload("t", "f32", 2, 3, 50, 60, 64, False, False, 1.0, 1.0, 9)
+    a, b = inputs.make_grad_out(w), inputs.make_grad_out(w)
+    assert a.shape == (2, 3, 50, 64) and np.array_equal(a, b)
+    assert not np.array_equal(a, inputs.make_inputs(w)["q"])
+    assert abs(float(a.mean())) < 0.05 and abs(float(a.std()) - 1.0) < 0.05

@@ -1,10 +1,11 @@
-"""Python binding of the C ABI in include/attn_fwd.h (argument marshalling only).
+"""Python binding of the C ABI in include/attn_fwd.h and include/attn_bwd.h (argument
+marshalling only).
 
-`attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size` and
-`attn_status_str` mirror the C entry points one to one (raw device pointers, sizes, a stream
-handle).  `fwd` and `decode` are the tensor-level conveniences: they check the tensors on the
-host, allocate O, LSE (and the decode workspace) with torch on the current stream and call
-`attn_fwd` / `attn_fwd_window` / `attn_decode`.  Every step of
+`attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size`, `attn_bwd`,
+`attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one to one (raw
+device pointers, sizes, a stream handle).  `fwd`, `decode` and `bwd` are the tensor-level
+conveniences: they check the tensors on the host, allocate the outputs (and workspaces) with
+torch on the current stream and call the matching entry point.  Every step of
 the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
 module raises instead of computing anything itself.
 """
@@ -25,7 +26,7 @@ STATUS = {
     -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size",
-           "attn_status_str")
+           "attn_bwd", "attn_bwd_workspace_size", "attn_status_str")
 
 _lib = None
 
@@ -66,6 +67,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     ]
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+        ctypes.c_void_p,
+    ]
+    lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
     lib.attn_status_str.restype = ctypes.c_char_p
     lib.attn_status_str.argtypes = [ctypes.c_int]
     _lib = lib
@@ -94,6 +105,17 @@ def attn_decode(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype
 
 def attn_decode_workspace_size(B, H, Nq, Nk, D, dtype) -> int:
     return int(load_library().attn_decode_workspace_size(B, H, Nq, Nk, D, dtype))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, key_lens,
+             dtype, workspace, workspace_bytes, stream) -> int:
+    """The C entry point of the backward (dQ, dK, dV from dO and the forward's O and LSE)."""
+    return load_library().attn_bwd(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale,
+                                   causal, key_lens, dtype, workspace, workspace_bytes, stream)
+
+
+def attn_bwd_workspace_size(B, H, Nq) -> int:
+    return int(load_library().attn_bwd_workspace_size(B, H, Nq))
 
 
 def attn_status_str(status: int) -> str:
@@ -210,3 +232,43 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
     if rc != ATTN_OK:
         raise AttnError(rc)
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: float | None = None,
+        dlse=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of attention(q, k, v) for the gradient `dout` of O (and `dlse` of LSE, or None).
+    o and lse are the forward's outputs for the same q, k, v, causal, key_lens and scale.
+    Tensors as for fwd (bf16 or fp16); returns (dq, dk, dv) in q's dtype."""
+    torch = _torch()
+    B, H, Nq, Nk, D, code, scale, kl_ptr, out, lse_t, handle = _check(q, k, v, key_lens, scale, o, lse,
+                                                                       stream)
+    if out is not o or lse_t is not lse:
+        raise ValueError("o and lse must be the forward's outputs")
+    if code == ATTN_F32:
+        raise ValueError("the backward takes bfloat16 or float16 tensors")
+    if not isinstance(dout, torch.Tensor) or dout.shape != q.shape or dout.dtype != q.dtype \
+            or dout.device != q.device or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous tensor like q")
+    if dlse is not None and (not isinstance(dlse, torch.Tensor) or tuple(dlse.shape) != (B, H, Nq)
+                             or dlse.dtype != torch.float32 or dlse.device != q.device
+                             or not dlse.is_contiguous()):
+        raise ValueError("dlse must be a contiguous float32 tensor [B, H, Nq] or None")
+    outs = []
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if t is None:
+            t = torch.empty_like(like)
+        elif t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like its input")
+        outs.append(t)
+    need = attn_bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
+    rc = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                  None if dlse is None else dlse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
+                  outs[2].data_ptr(), B, H, Nq, Nk, D, scale, int(bool(causal)), kl_ptr, code,
+                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), handle)
+    if rc != ATTN_OK:
+        raise AttnError(rc)
+    return tuple(outs)

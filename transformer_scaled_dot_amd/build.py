@@ -12,8 +12,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_fwd.so")
-SOURCES = ["attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
-HEADERS = ["attn_common.h", os.path.join(ROOT, "include", "attn_fwd.h")]
+SOURCES = ["attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip",
+           "attn_bwd_api.hip", "attn_bwd_mfma.hip"]
+HEADERS = ["attn_common.h", "attn_bwd.h", os.path.join(ROOT, "include", "attn_fwd.h"),
+           os.path.join(ROOT, "include", "attn_bwd.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,533 @@
+// attn_bwd_mfma.hip -- attention backward (dQ, dK, dV) for bf16 / fp16 on gfx950 matrix cores.
+//
+// The gradients of O = softmax(scale Q K^T + mask) V and LSE, given dO and dLSE, are
+//   P  = exp(scale Q K^T - LSE)          (rebuilt from the forward's LSE, never stored)
+//   dV = P^T dO,  dP = dO V^T,  Dr_i = rowsum(dO * O)_i - dLSE_i,  dS = P * (dP - Dr)
+//   dQ = scale dS K,  dK = scale dS^T Q
+// -- the backward that rebuilds the softmax output from the forward's statistics instead of
+// keeping the N x N matrix (hotelren.com page on attention, sec.4.2; aicoding.csdn.net page,
+// ch.1: the backward needs the softmax output).  Two kernels, no atomics:
+//
+//   attn_bwd_dq_kernel   one workgroup per 128-row Q tile (lane = query, as in the forward):
+//                        Dr for its rows (written to the workspace), then for every visible
+//                        64-key K/V tile  S^T = K Q^T,  dP^T = V dO^T,  dQ^T += K^T dS^T.
+//   attn_bwd_dkdv_kernel one workgroup per 128-key tile (lane = key): K and V stay in registers,
+//                        32-row Q/dO tiles stream through LDS;  S = Q K^T,  dP = dO V^T,
+//                        dV^T += dO^T P,  dK^T += Q^T dS.
+//
+// Each streamed tile is read both by rows (A operand of the score-like products) and
+// transposed (A operand of the gradient products, LDS transpose read), so its 16-byte chunks are
+// XOR-swizzled with one function of the row that keeps both access patterns free of bank
+// conflicts.  Every product runs on v_mfma_f32_32x32x16 with fp32 accumulation; the rows of the
+// streamed A operand are fed with bits 2 and 3 of the row index swapped, so the accumulator of
+// S (or dP) already has the B-operand layout of the next product, as in the forward kernel.
+#include "attn_bwd.h"
+#include "attn_common.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+    using vec8 = bf16x8_t;
+    static __device__ __forceinline__ f32x16_t mma(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<_Float16> {
+    using vec8 = f16x8_t;
+    static __device__ __forceinline__ f32x16_t mma(vec8 a, vec8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int NT = 256;    // threads per workgroup (4 waves)
+constexpr int BMQ = 128;   // dQ kernel: query rows per workgroup
+constexpr int BNQ = 64;    // dQ kernel: keys per K/V tile
+constexpr int BNK = 128;   // dK/dV kernel: keys per workgroup
+constexpr int BMK = 32;    // dK/dV kernel: query rows per Q/dO tile
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
+
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Chunk swizzle of a tile row that serves both the row read (32 rows, one chunk column per
+// half-wave) and the transpose read (4 consecutive rows x 2 chunks per 16 lanes): for D = 128
+// the two 2-bit halves of (row mod 16) are swapped into the chunk index; for D = 64 (8 chunks)
+// bit 1 of the row flips chunk bit 2 and bits 2-3 of the row flip chunk bits 0-1.
+template <int D>
+__device__ __forceinline__ int dswz(int row) {
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) ^ ((row >> 2) & 3));
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// One lane's 8 elements of a [rows, D] slice: row `row`, columns c0 .. c0+7 (zeros past `bytes`).
+__device__ __forceinline__ u32x4_t load8(const void* base, int bytes, int off_bytes) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferWord3);
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off_bytes, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------ dQ
+template <typename T, int D>
+__global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using M = Mma<T>;
+    using vec8 = typename M::vec8;
+    constexpr int BN = BNQ;
+    constexpr int NCH = D / 8;              // 16-byte chunks per row
+    constexpr int KSTEPS = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int KT = BN / 32;
+    constexpr int RB = D * 2;               // bytes per row
+    constexpr int CPT = BN * NCH / NT;      // chunks per thread per tile
+    constexpr int TILE = BN * RB;
+    constexpr int STAGE = 2 * TILE;         // K tile then V tile
+    static_assert(CPT >= 1, "tile too small for the workgroup");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * STAGE];
+    lds_u8* const smem = (lds_u8*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, g = lane >> 5;
+
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_q);
+    const int bh = blk / p.n_qtiles;
+    int qt = blk - bh * p.n_qtiles;
+    if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
+    const int b = bh / p.H;
+    const int q0 = qt * BMQ;
+    const int qw0 = q0 + wave * 32;
+    const int qi = qw0 + r;
+    const bool row_ok = qi < p.Nq;
+    const bool wave_has_rows = qw0 < p.Nq;
+
+    const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
+    const int q_last = min(p.Nq, q0 + BMQ) - 1;
+    const int kv_end = p.causal ? min(kv_valid, q_last + 1) : kv_valid;
+    const int n_tiles = (kv_end + BN - 1) / BN;
+
+    const size_t qbase = (size_t)bh * p.Nq * D;
+    const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
+    const T* vg = (const T*)p.v + (size_t)bh * p.Nk * D;
+    const int qbytes = p.Nq * D * 2;
+
+    // Q^T and dO^T operands: lane (r, g) holds row qi, columns 16 ks + 8 g .. +7; Dr from O.
+    vec8 qf[KSTEPS], df[KSTEPS];
+    float dr_part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int off = (qi * D + 16 * ks + 8 * g) * 2;
+        u32x4_t xq = load8((const T*)p.q + qbase, qbytes, off);
+        if (p.negate) xq ^= 0x80008000u;
+        qf[ks] = __builtin_bit_cast(vec8, xq);
+        df[ks] = __builtin_bit_cast(vec8, load8((const T*)p.dout + qbase, qbytes, off));
+        const vec8 of = __builtin_bit_cast(vec8, load8((const T*)p.o + qbase, qbytes, off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dr_part = __builtin_fmaf(to_f(df[ks][e]), to_f(of[e]), dr_part);
+    }
+    float dr = dr_part + __shfl_xor(dr_part, 32);
+    float lse2 = INFINITY;  // rows past Nq (and rows that see no key) get P = 0
+    if (row_ok) {
+        const size_t ri = (size_t)bh * p.Nq + qi;
+        if (p.dlse) dr -= p.dlse[ri];
+        const float l = p.lse[ri];
+        if (l != -INFINITY) lse2 = l * kLog2e;
+    }
+    if (g == 0 && qi < p.nq_pad) {
+        const size_t si = (size_t)bh * p.nq_pad + qi;
+        p.stats[si] = lse2;
+        p.stats[(size_t)p.B * p.H * p.nq_pad + si] = dr;
+    }
+
+    // DMA offsets: slot (i*NT + tid) of a tile holds global chunk (row, chunk ^ dswz(row)).
+    int toff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int s = i * NT + tid;
+        const int row = s / NCH, phys = s % NCH;
+        toff[i] = (row * D + (phys ^ dswz<D>(row)) * 8) * 2;
+    }
+    auto issue_tile = [&](const int tile, const int stage) {
+        const int j0 = tile * BN;
+        const int bytes = (kv_valid - j0) * D * 2;  // keys past the valid length arrive as zeros
+        const __amdgpu_buffer_rsrc_t krs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* kd = smem + stage * STAGE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kd, 16, toff[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* vd = smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vd, 16, toff[i], 0, 0, 0);
+        }
+    };
+
+    // Row reads (A of S^T and dP^T): row swap23(r) (+32 kt), chunk (2 ks + g) ^ dswz.
+    int raddr[KSTEPS];
+    {
+        const int row = swap23(r);
+        const int sw = dswz<D>(row);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = row * RB + (((2 * ks + g) ^ sw) * 16);
+    }
+    // Transpose reads (A of dQ^T = K^T dS^T): lane s of a 16-lane group names 8 bytes of row
+    // 8 g + s/4 (+4 for the upper half, +16 h16) at columns 32 dt + 16 G + 4 (s & 3).
+    int taddr_lo[DT], taddr_hi[DT];
+    {
+        const int s = lane & 15, G1 = (lane >> 4) & 1;
+        const int rlo = 8 * g + (s >> 2), rhi = rlo + 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int c = 4 * dt + 2 * G1 + ((s & 3) >> 1);
+            taddr_lo[dt] = rlo * RB + ((c ^ dswz<D>(rlo)) * 16) + 8 * (s & 1);
+            taddr_hi[dt] = rhi * RB + ((c ^ dswz<D>(rhi)) * 16) + 8 * (s & 1);
+        }
+    }
+
+    f32x16_t acc[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) acc[t] = f32x16_t{};
+    const float c2 = p.scale_log2;
+
+    auto do_tile = [&](const int it, const int stage) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
+
+        const int j0 = it * BN;
+        if (!wave_has_rows || (p.causal && j0 > qw0 + 31)) return;
+        const lds_u8* kb = smem + stage * STAGE;
+        const lds_u8* vb = kb + TILE;
+
+        f32x16_t s[KT], dp[KT];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            s[kt] = f32x16_t{};
+            dp[kt] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const u32x4_t a = *(const lds_u32x4*)(kb + raddr[ks] + kt * 32 * RB);
+                s[kt] = M::mma(__builtin_bit_cast(vec8, a), qf[ks], s[kt]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const u32x4_t a = *(const lds_u32x4*)(vb + raddr[ks] + kt * 32 * RB);
+                dp[kt] = M::mma(__builtin_bit_cast(vec8, a), df[ks], dp[kt]);
+            }
+        }
+
+        // Register i of s[kt] / dp[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.
+        const bool need_mask = j0 + BN > kv_valid || (p.causal && j0 + BN - 1 > qw0);
+        vec8 dsb[BN / 16];
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -lse2));
+                if (need_mask) {
+                    const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
+                    if (j >= kv_valid || (p.causal && j > qi)) pv = 0.f;
+                }
+                dsb[2 * kt + (i >> 3)][i & 7] = (T)(pv * (dp[kt][i] - dr));
+            }
+
+        // dQ^T += K^T dS^T, 16 keys per MFMA
+#pragma unroll
+        for (int h16 = 0; h16 < BN / 16; ++h16) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + taddr_lo[t] + 16 * h16 * RB));
+                const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kb + taddr_hi[t] + 16 * h16 * RB));
+                const vec8 a = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0],
+                                                                 __builtin_bit_cast(u32x2_t, lo)[1],
+                                                                 __builtin_bit_cast(u32x2_t, hi)[0],
+                                                                 __builtin_bit_cast(u32x2_t, hi)[1]});
+                acc[t] = M::mma(a, dsb[h16], acc[t]);
+            }
+        }
+    };
+
+    if (n_tiles > 0) issue_tile(0, 0);
+    for (int it = 0; it < n_tiles; it += 2) {
+        do_tile(it, 0);
+        if (it + 1 < n_tiles) do_tile(it + 1, 1);
+    }
+
+    // dQ = scale * acc; accumulator registers 4a..4a+3 of acc[t] hold dQ[qi][32 t + 8 a + 4 g + 0..3]
+    if (row_ok) {
+        T* dqg = (T*)p.dq + qbase + (size_t)qi * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                u32x2_t w;
+                w[0] = (unsigned)__builtin_bit_cast(unsigned short, (T)(acc[t][4 * a + 0] * sc)) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(acc[t][4 * a + 1] * sc)) << 16);
+                w[1] = (unsigned)__builtin_bit_cast(unsigned short, (T)(acc[t][4 * a + 2] * sc)) |
+                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(acc[t][4 * a + 3] * sc)) << 16);
+                *(u32x2_t*)(dqg + 32 * t + 8 * a + 4 * g) = w;
+            }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// ---------------------------------------------------------------------------------- dK, dV
+template <typename T, int D>
+__global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using M = Mma<T>;
+    using vec8 = typename M::vec8;
+    constexpr int BM = BMK;                 // query rows per streamed tile
+    constexpr int NCH = D / 8;
+    constexpr int KSTEPS = D / 16;
+    constexpr int DT = D / 32;
+    constexpr int RB = D * 2;
+    constexpr int CPT = BM * NCH / NT;
+    constexpr int TILE = BM * RB;
+    constexpr int STAGE = 2 * TILE;         // Q tile then dO tile
+    static_assert(CPT >= 1, "tile too small for the workgroup");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * STAGE];
+    lds_u8* const smem = (lds_u8*)smem_raw;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, g = lane >> 5;
+
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_k);
+    const int bh = blk / p.n_ktiles;
+    const int kt_idx = blk - bh * p.n_ktiles;
+    const int b = bh / p.H;
+    const int k0 = kt_idx * BNK;
+    const int kw0 = k0 + wave * 32;
+    const int kj = kw0 + r;  // this lane's key
+
+    const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
+    const size_t kbase = (size_t)bh * p.Nk * D;
+    const int kbytes = p.Nk * D * 2;
+    const size_t qbase = (size_t)bh * p.Nq * D;
+    const T* qg = (const T*)p.q + qbase;
+    const T* dog = (const T*)p.dout + qbase;
+
+    // Query tiles [t_begin, n_tiles) hold every row that may see a key of this workgroup.
+    const int n_tiles = k0 < kv_valid ? (p.Nq + BM - 1) / BM : 0;
+    const int t_begin = p.causal ? min(k0, p.Nq) / BM : 0;
+    const bool wave_has_keys = kw0 < kv_valid;
+
+    // K^T and V^T operands: lane (r, g) holds key kj, columns 16 ks + 8 g .. +7.
+    vec8 kf[KSTEPS], vf[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int off = (kj * D + 16 * ks + 8 * g) * 2;
+        u32x4_t xk = load8((const T*)p.k + kbase, kbytes, off);
+        if (p.negate) xk ^= 0x80008000u;
+        kf[ks] = __builtin_bit_cast(vec8, xk);
+        vf[ks] = __builtin_bit_cast(vec8, load8((const T*)p.v + kbase, kbytes, off));
+    }
+
+    int toff[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int s = i * NT + tid;
+        const int row = s / NCH, phys = s % NCH;
+        toff[i] = (row * D + (phys ^ dswz<D>(row)) * 8) * 2;
+    }
+    auto issue_tile = [&](const int tile, const int stage) {
+        const int i0 = tile * BM;
+        const int bytes = (p.Nq - i0) * D * 2;  // rows past Nq arrive as zeros
+        const __amdgpu_buffer_rsrc_t qrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(qg + (size_t)i0 * D), 0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t drs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(dog + (size_t)i0 * D), 0, bytes, kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* qd = smem + stage * STAGE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)qd, 16, toff[i], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            lds_u8* dd = smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)dd, 16, toff[i], 0, 0, 0);
+        }
+    };
+
+    int raddr[KSTEPS];
+    {
+        const int row = swap23(r);
+        const int sw = dswz<D>(row);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) raddr[ks] = row * RB + (((2 * ks + g) ^ sw) * 16);
+    }
+    int taddr_lo[DT], taddr_hi[DT];
+    {
+        const int s = lane & 15, G1 = (lane >> 4) & 1;
+        const int rlo = 8 * g + (s >> 2), rhi = rlo + 4;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int c = 4 * dt + 2 * G1 + ((s & 3) >> 1);
+            taddr_lo[dt] = rlo * RB + ((c ^ dswz<D>(rlo)) * 16) + 8 * (s & 1);
+            taddr_hi[dt] = rhi * RB + ((c ^ dswz<D>(rhi)) * 16) + 8 * (s & 1);
+        }
+    }
+
+    f32x16_t dka[DT], dva[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+        dka[t] = f32x16_t{};
+        dva[t] = f32x16_t{};
+    }
+    const float c2 = p.scale_log2;
+    // this slice's rows of the two statistics planes (padded to whole 32-row tiles)
+    const float* lse2g = p.stats + (size_t)bh * p.nq_pad;
+    const float* drg = lse2g + (size_t)p.B * p.H * p.nq_pad;
+
+    auto do_tile = [&](const int it, const int stage) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
+
+        const int i0 = it * BM;
+        // nothing of this tile reaches the wave's keys
+        if (!wave_has_keys || (p.causal && i0 + BM - 1 < kw0)) return;
+        const lds_u8* qb = smem + stage * STAGE;
+        const lds_u8* db = qb + TILE;
+
+        // Row statistics of the tile: register i of the accumulators holds query
+        // i0 + 16 (i/8) + 8 g + i%8, so a lane needs rows i0 + 8 g + 0..7 and i0 + 16 + 8 g + 0..7.
+        f32x4_t ls[4], rs[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int row = i0 + 16 * h + 8 * g + 4 * u;  // < nq_pad: i0 + 32 <= nq_pad
+                ls[2 * h + u] = *(const f32x4_t*)(lse2g + row);
+                rs[2 * h + u] = *(const f32x4_t*)(drg + row);
+            }
+
+        // S = Q K^T and dP = dO V^T (32 queries x 32 keys of this wave)
+        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4_t a = *(const lds_u32x4*)(qb + raddr[ks]);
+            s = M::mma(__builtin_bit_cast(vec8, a), kf[ks], s);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const u32x4_t a = *(const lds_u32x4*)(db + raddr[ks]);
+            dp = M::mma(__builtin_bit_cast(vec8, a), vf[ks], dp);
+        }
+
+        // Rows past Nq carry an LSE of +inf, so their weights are already 0.
+        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0);
+        vec8 pb[2], dsb[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float dr = rs[i >> 2][i & 3];
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -ls[i >> 2][i & 3]));
+            if (need_mask) {
+                const int qrow = i0 + 16 * (i >> 3) + 8 * g + (i & 7);
+                if (kj >= kv_valid || (p.causal && kj > qrow)) pv = 0.f;
+            }
+            pb[i >> 3][i & 7] = (T)pv;
+            dsb[i >> 3][i & 7] = (T)(pv * (dp[i] - dr));
+        }
+
+        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+#pragma unroll
+        for (int h16 = 0; h16 < 2; ++h16) {
+#pragma unroll
+            for (int t = 0; t < DT; ++t) {
+                const s16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_lo[t] + 16 * h16 * RB));
+                const s16x4_t dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_hi[t] + 16 * h16 * RB));
+                const vec8 ad = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, dlo)[0],
+                                                                  __builtin_bit_cast(u32x2_t, dlo)[1],
+                                                                  __builtin_bit_cast(u32x2_t, dhi)[0],
+                                                                  __builtin_bit_cast(u32x2_t, dhi)[1]});
+                dva[t] = M::mma(ad, pb[h16], dva[t]);
+                const s16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_lo[t] + 16 * h16 * RB));
+                const s16x4_t qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_hi[t] + 16 * h16 * RB));
+                const vec8 aq = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, qlo)[0],
+                                                                  __builtin_bit_cast(u32x2_t, qlo)[1],
+                                                                  __builtin_bit_cast(u32x2_t, qhi)[0],
+                                                                  __builtin_bit_cast(u32x2_t, qhi)[1]});
+                dka[t] = M::mma(aq, dsb[h16], dka[t]);
+            }
+        }
+    };
+
+    if (t_begin < n_tiles) issue_tile(t_begin, 0);
+    for (int it = t_begin; it < n_tiles; it += 2) {
+        do_tile(it, 0);
+        if (it + 1 < n_tiles) do_tile(it + 1, 1);
+    }
+
+    // dK = scale * dka, dV = dva; registers 4a..4a+3 of [t] hold column 32 t + 8 a + 4 g + 0..3
+    if (kj < p.Nk) {
+        T* dkg = (T*)p.dk + kbase + (size_t)kj * D;
+        T* dvg = (T*)p.dv + kbase + (size_t)kj * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                u32x2_t wk, wv;
+                wk[0] = (unsigned)__builtin_bit_cast(unsigned short, (T)(dka[t][4 * a + 0] * sc)) |
+                        ((unsigned)__builtin_bit_cast(unsigned short, (T)(dka[t][4 * a + 1] * sc)) << 16);
+                wk[1] = (unsigned)__builtin_bit_cast(unsigned short, (T)(dka[t][4 * a + 2] * sc)) |
+                        ((unsigned)__builtin_bit_cast(unsigned short, (T)(dka[t][4 * a + 3] * sc)) << 16);
+                wv[0] = (unsigned)__builtin_bit_cast(unsigned short, (T)dva[t][4 * a + 0]) |
+                        ((unsigned)__builtin_bit_cast(unsigned short, (T)dva[t][4 * a + 1]) << 16);
+                wv[1] = (unsigned)__builtin_bit_cast(unsigned short, (T)dva[t][4 * a + 2]) |
+                        ((unsigned)__builtin_bit_cast(unsigned short, (T)dva[t][4 * a + 3]) << 16);
+                *(u32x2_t*)(dkg + 32 * t + 8 * a + 4 * g) = wk;
+                *(u32x2_t*)(dvg + 32 * t + 8 * a + 4 * g) = wv;
+            }
+    }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <typename T, int D>
+hipError_t launch_one(const attn::BwdParams& p, hipStream_t stream) {
+    attn::BwdParams pc = p;
+    void* args[] = {&pc};
+    hipError_t e = hipLaunchKernel((const void*)attn_bwd_dq_kernel<T, D>, dim3(p.n_blocks_q), dim3(NT),
+                                   args, 0, stream);
+    if (e != hipSuccess) return e;
+    return hipLaunchKernel((const void*)attn_bwd_dkdv_kernel<T, D>, dim3(p.n_blocks_k), dim3(NT), args,
+                           0, stream);
+}
+
+}  // namespace
+
+int attn_bwd_q_block() { return BMQ; }
+int attn_bwd_k_block() { return BNK; }
+
+hipError_t attn_launch_bwd_mfma(const attn::BwdParams& p, int dtype, int D, hipStream_t stream) {
+    if (dtype == 2) return D == 128 ? launch_one<__bf16, 128>(p, stream) : launch_one<__bf16, 64>(p, stream);
+    return D == 128 ? launch_one<_Float16, 128>(p, stream) : launch_one<_Float16, 64>(p, stream);
+}

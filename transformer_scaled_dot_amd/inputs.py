@@ -8,8 +8,9 @@ Recipe (one stream per tensor, all counter-based so any slice can be regenerated
 * SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number generators",
   OOPSLA 2014): output n >= 1 of a stream with start state s is mix(s + n*G mod 2^64),
   G = 0x9E3779B97F4A7C15, mix = the published two xor-shift-multiply rounds.
-* The stream for tensor t (0 = Q, 1 = K, 2 = V, 3 = key lengths) starts at state
-  mix(seed + (t+1)*G), i.e. the t-th output of the seed's own stream.
+* The stream for tensor t (0 = Q, 1 = K, 2 = V, 3 = key lengths, 4 = dO, the gradient of O
+  fed to the backward, N(0, 1)) starts at state mix(seed + (t+1)*G), i.e. the t-th output of
+  the seed's own stream.
 * Uniforms: u = (x >> 11) * 2^-53 in [0, 1).
 * Normals: Box-Muller on consecutive pairs (u1, u2): r = sqrt(-2 ln(1 - u1)),
   z0 = r cos(2 pi u2), z1 = r sin(2 pi u2), in float64.
@@ -227,6 +228,12 @@ def make_tensor(seed: int, which: int, shape, sigma: float, dtype: str) -> np.nd
     if sigma != 1.0:
         z *= sigma
     return to_storage(z, dtype).reshape(shape)
+
+
+def make_grad_out(w: Workload, seed: int | None = None) -> np.ndarray:
+    """dO for the backward: N(0, 1) in the storage dtype, [B, H, Nq, D] (stream 4)."""
+    s = w.seed if seed is None else seed
+    return make_tensor(s, 4, (w.B, w.H, w.Nq, w.D), 1.0, w.dtype)
 
 
 def make_inputs(w: Workload, seed: int | None = None) -> dict:
