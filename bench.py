@@ -1,10 +1,11 @@
 """Benchmark: fused attention forward on one MI355X, long-context causal workload by default.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--no-cpu-baseline]
 
 One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
 resident in HBM; attn_decode, key splits and merge, for the KV-cache decode workloads, whose
-line reports HBM GB/s against the 8 TB/s peak instead of TFLOP/s).  W untimed warm-up steps, then K timed steps bracketed by device
+line reports HBM GB/s against the 8 TB/s peak instead of TFLOP/s; with --pass bwd, one call of
+attn_bwd, both of its kernels, on the forward's O and LSE and a seeded dO).  W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation, timed with HIP events recorded on the stream the kernel is launched on.
 Prints ONE JSON line on stdout (everything else goes to stderr).
 
@@ -29,19 +30,21 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·D, causal halved) and % of bf16 MFMA peak"
 METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4·D per (query, key) pair inside the band)"
 METRIC_DECODE = "KV-cache decode attention HBM GB/s (Q, valid K/V rows, O and LSE bytes per step)"
+METRIC_BWD = "attention bwd TFLOP/s (2.5 x the forward's 4·B·H·N²·D, causal halved: five N²·D products)"
 # MI355X published dense peaks (256 CUs at 2.4 GHz).
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["attn_common.h", "attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
+BWD_KERNEL_SOURCES = ["attn_common.h", "attn_bwd.h", "attn_bwd_api.hip", "attn_bwd_mfma.hip"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for fn in KERNEL_SOURCES:
+    for fn in sources:
         with open(os.path.join(ROOT, "transformer_scaled_dot_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -68,6 +71,62 @@ def algorithmic_bytes(w, key_lens=None) -> float:
     kv_rows = w.B * w.Nk if key_lens is None else \
         int(sum(min(max(int(n), 0), w.Nk) for n in key_lens))
     return eb * (2 * w.B * w.H * w.Nq * w.D + 2 * w.H * kv_rows * w.D) + 4 * w.B * w.H * w.Nq
+
+
+def bwd_algorithmic_bytes(w) -> float:
+    """Backward: read Q, K, V, O, dO and LSE once, write dQ, dK, dV once."""
+    eb = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    nq, nk = w.B * w.H * w.Nq * w.D, w.B * w.H * w.Nk * w.D
+    return eb * (4 * nq + 4 * nk) + 4 * w.B * w.H * w.Nq
+
+
+def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
+    """Time the oracle's backward on whole (b, h) slices (random, growing until ~target_s / 2)."""
+    import numpy as np
+
+    import oracle
+
+    impl = oracle.default()
+    cores = impl.max_threads()
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(w.B * w.H)
+    args = (x["q"], x["k"], x["v"], do, w.dtype, float(x["scale"]), w.causal, x["key_lens"])
+    n, spent, done = 1, 0.0, []
+    while True:
+        sel = order[len(done):len(done) + n]
+        if sel.size == 0:
+            break
+        t0 = time.perf_counter()
+        want = impl.attn_bwd(*args, None, sel)
+        spent += time.perf_counter() - t0
+        done.append((sel, want))
+        if spent >= 0.5 * target_s:
+            break
+        n = max(1, min(16, n * 2))
+    slices = np.concatenate([d[0] for d in done])
+    kl = x["key_lens"]
+    pairs = 0
+    for bh in slices:
+        L = w.Nk if kl is None else int(np.clip(kl[bh // w.H], 0, w.Nk))
+        i = np.arange(w.Nq)
+        pairs += int(np.minimum(L, i + 1).sum()) if w.causal else w.Nq * L
+    flops = 2.5 * 4.0 * w.D * pairs
+    errs = []
+    for sel, want in done:
+        for name, got, ref in zip(("dq", "dk", "dv"), grads, want):
+            g = got.detach().reshape(-1, *got.shape[2:])[np.asarray(sel)].double().cpu().numpy()
+            errs.append(float(np.max(np.abs(g - ref)) / max(float(np.max(np.abs(ref))), 1e-30)))
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{slices.size} random (b, h) slices of the same workload (seed {seed}), fp64 oracle "
+                  f"backward with {cores} OpenMP threads, {spent:.2f} s; flops counted as 2.5 x 4*D per "
+                  f"visible (query, key) pair, as in the metric",
+        "seconds": spent,
+        "sample_max_rel_err_grads": max(errs),
+    }
 
 
 def oracle_causal(w) -> int:
@@ -160,6 +219,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward (attn_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -211,7 +272,26 @@ def main():
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr())
     dims = (w.B, w.H, w.Nq, w.Nk, w.D, scale, int(w.causal))
     lib = binding.load_library()
-    if w.kv_cache:
+    bwd = a.which == "bwd"
+    if bwd:
+        if w.kv_cache or w.window is not None or w.dtype == "f32":
+            raise SystemExit(f"bench.py: the backward takes bf16/fp16 workloads without a window or KV cache ({name})")
+        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream)
+        do_np = inputs.make_grad_out(w)
+        do = to_dev(do_np)
+        grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        ws_bytes = binding.attn_bwd_workspace_size(w.B, w.H, w.Nq)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        binding.bwd(q, k, v, o, lse, do, causal=w.causal, key_lens=kl, scale=scale, dq=grads[0],
+                    dk=grads[1], dv=grads[2], workspace=workspace, stream=stream)
+        args = (*ptrs[:4], do.data_ptr(), lse.data_ptr(), None, *(t.data_ptr() for t in grads), *dims,
+                kl_ptr, code, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+
+        def step():
+            rc = lib.attn_bwd(*args)
+            if rc != binding.ATTN_OK:
+                raise binding.AttnError(rc)
+    elif w.kv_cache:
         ws_bytes = binding.attn_decode_workspace_size(w.B, w.H, w.Nq, w.Nk, w.D, code)
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         log(f"[bench] decode workspace {ws_bytes} bytes")
@@ -271,12 +351,21 @@ def main():
         log(f"[bench] calibration copy: {a.calib_copy_mib} MiB read + {a.calib_copy_mib} MiB written")
         del src, dst
 
-    flops = w.flops()
+    flops = w.flops() * (2.5 if bwd else 1.0)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    src_hash = kernel_source_hash()
-    traffic = read_traffic(name, src_hash, "attn_decode" if w.kv_cache else "attn_fwd")
-    abytes = algorithmic_bytes(w, x["key_lens"])
-    if w.kv_cache:
+    src_hash = kernel_source_hash(BWD_KERNEL_SOURCES if bwd else KERNEL_SOURCES)
+    family = "attn_bwd" if bwd else ("attn_decode" if w.kv_cache else "attn_fwd")
+    traffic = read_traffic(name, src_hash, family)
+    abytes = bwd_algorithmic_bytes(w) if bwd else algorithmic_bytes(w, x["key_lens"])
+    if bwd:
+        metric, unit = METRIC_BWD, "TFLOP/s"
+        value = tflops
+        achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": traffic,
+                    "kernels": "attn_bwd_dq_kernel + attn_bwd_dkdv_kernel, timed together"}
+    elif w.kv_cache:
         # HBM-bound: K and V are read once and each byte feeds 2 flops per query.
         metric, unit = METRIC_DECODE, "GB/s"
         value = abytes / (ms_per_step * 1e-3) / 1e9
@@ -308,7 +397,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
                    "causal": w.causal, "key_padding": w.padded, "window": w.window,
-                   "kv_cache": w.kv_cache, "seed": x["seed"], "parallelism": "none (1 GPU)"},
+                   "kv_cache": w.kv_cache, "pass": a.which, "seed": x["seed"],
+                   "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "roofline": roofline,
         "tflops": tflops,
@@ -318,7 +408,13 @@ def main():
         "kernel_source_sha256": src_hash,
         "input_sha256": inputs.input_hashes(x),
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and bwd:
+        log(f"[bench] cpu baseline: oracle backward on sampled slices (~{a.cpu_seconds:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline_bwd(w, x, do_np, grads, a.cpu_seconds)
+        cb = result["cpu_baseline"]
+        log(f"[bench] cpu baseline {cb['value']:.4g} {cb['unit']} on {cb['cores']} threads; "
+            f"sample max relative gradient error {cb['sample_max_rel_err_grads']:.3e}")
+    elif not a.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on a sample (~{a.cpu_seconds:.0f} s)")
         result["cpu_baseline"] = cpu_baseline(w, x, o, lse, a.cpu_seconds)
         cb = result["cpu_baseline"]

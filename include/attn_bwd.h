@@ -49,7 +49,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes attn_bwd needs: 2 * B * H * round_up(Nq, 32) * 4; 0 for B, H or Nq < 1. */
+/* Workspace bytes attn_bwd needs: 2 * B * H * round_up(Nq, 64) * 4; 0 for B, H or Nq < 1.
+ * attn_bwd returns ATTN_ERR_SHAPE when this exceeds 2^31 - 1 bytes. */
 size_t attn_bwd_workspace_size(int B, int H, int Nq);
 
 #ifdef __cplusplus

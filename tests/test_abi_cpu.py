@@ -149,6 +149,7 @@ BWD_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dlse=None, dq=F
     (dict(scale=float("nan")), -5), (dict(causal=2), -6), (dict(dq=FAKE + 4), -8),
     (dict(dlse=FAKE + 4), -8), (dict(key_lens=FAKE + 1), -8), (dict(ws=None), -1),
     (dict(ws=FAKE + 8), -8), (dict(ws_bytes=2 * 2 * 3 * 64 * 4 - 1), -10), (dict(Nq=1 << 22, D=128), -2),
+    (dict(B=4096, H=64, Nq=1024, D=64, ws_bytes=1 << 40), -2),
 ])
 def test_host_validation_bwd(over, code):
     """attn_bwd checks every argument on the host before anything is enqueued."""
@@ -161,9 +162,10 @@ def test_host_validation_bwd(over, code):
 
 
 def test_bwd_workspace_size():
-    """Two fp32 planes of [B, H, Nq rounded up to 32]; 0 for an empty shape."""
+    """Two fp32 planes of [B, H, Nq rounded up to 64]; 0 for an empty shape."""
     ws = binding.attn_bwd_workspace_size
     assert ws(2, 3, 40) == 2 * 2 * 3 * 64 * 4
-    assert ws(1, 1, 32) == 2 * 32 * 4
+    assert ws(1, 1, 32) == 2 * 64 * 4
+    assert ws(1, 1, 65) == 2 * 128 * 4
     assert ws(1, 32, 16384) == 2 * 32 * 16384 * 4
     assert ws(0, 1, 1) == 0 and ws(1, 0, 1) == 0 and ws(1, 1, 0) == 0

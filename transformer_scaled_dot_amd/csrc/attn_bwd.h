@@ -18,7 +18,7 @@ struct BwdParams {
     void* dk;            // [B, H, Nk, D]
     void* dv;            // [B, H, Nk, D]
     // Workspace written by the dQ kernel and read by the dK/dV kernel: two planes of
-    // [B, H, nq_pad] fp32 (rows padded to a multiple of 32): LSE * log2(e) (+inf for a row that
+    // [B, H, nq_pad] fp32 (rows padded to a multiple of 64): LSE * log2(e) (+inf for a row that
     // sees no key and for padding rows), then Dr = rowsum(dO * O) - dLSE (0 on padding rows).
     float* stats;
     int nq_pad;

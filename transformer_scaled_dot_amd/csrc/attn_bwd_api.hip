@@ -7,7 +7,9 @@
 
 namespace {
 
-int64_t nq_padded(int Nq) { return ((int64_t)Nq + 31) / 32 * 32; }
+// Statistics rows are padded to whole 64-row tiles so the dK/dV kernel's tile reads stay
+// inside each (b, h) slice.
+int64_t nq_padded(int Nq) { return ((int64_t)Nq + 63) / 64 * 64; }
 
 }  // namespace
 
@@ -35,7 +37,8 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     const int64_t n_qtiles = ((int64_t)Nq + bm - 1) / bm, n_ktiles = ((int64_t)Nk + bn - 1) / bn;
     const int64_t nbq = n_qtiles * H * B, nbk = n_ktiles * H * B;
     const int64_t pad = nq_padded(Nq);
-    if (nbq > INT32_MAX || nbk > INT32_MAX || 2 * (int64_t)B * H * pad > INT32_MAX) return ATTN_ERR_SHAPE;
+    // the statistics planes are addressed with 32-bit byte offsets
+    if (nbq > INT32_MAX || nbk > INT32_MAX || 2 * (int64_t)B * H * pad * 4 > INT32_MAX) return ATTN_ERR_SHAPE;
 
     if (!workspace) return ATTN_ERR_NULL;
     if (((uintptr_t)workspace & 15) != 0) return ATTN_ERR_ALIGN;

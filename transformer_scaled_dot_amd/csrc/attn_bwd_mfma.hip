@@ -239,20 +239,30 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
             }
         }
 
-        // Register i of s[kt] / dp[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.
+        // Register i of s[kt] / dp[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.  The mask
+        // matters only on tiles that reach past the valid keys or the wave's first row.
         const bool need_mask = j0 + BN > kv_valid || (p.causal && j0 + BN - 1 > qw0);
+        if (need_mask) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
+                    const bool off = j >= kv_valid || (p.causal && j > qi);
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -lse2));
+                    s[kt][i] = off ? 0.f : pv;
+                }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -lse2));
+        }
         vec8 dsb[BN / 16];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -lse2));
-                if (need_mask) {
-                    const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
-                    if (j >= kv_valid || (p.causal && j > qi)) pv = 0.f;
-                }
-                dsb[2 * kt + (i >> 3)][i & 7] = (T)(pv * (dp[kt][i] - dr));
-            }
+            for (int i = 0; i < 16; ++i) dsb[2 * kt + (i >> 3)][i & 7] = (T)(s[kt][i] * (dp[kt][i] - dr));
 
         // dQ^T += K^T dS^T, 16 keys per MFMA
 #pragma unroll
@@ -302,14 +312,17 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
     using M = Mma<T>;
     using vec8 = typename M::vec8;
     constexpr int BM = BMK;                 // query rows per streamed tile
+    constexpr int QB = BM / 32;             // 32-row blocks per tile
     constexpr int NCH = D / 8;
     constexpr int KSTEPS = D / 16;
     constexpr int DT = D / 32;
     constexpr int RB = D * 2;
     constexpr int CPT = BM * NCH / NT;
     constexpr int TILE = BM * RB;
-    constexpr int STAGE = 2 * TILE;         // Q tile then dO tile
+    constexpr int SBYTES = 1024;            // row statistics: one 64-lane DMA of 16 bytes each
+    constexpr int STAGE = 2 * TILE + SBYTES;  // Q tile, dO tile, LSE * log2(e) and Dr of its rows
     static_assert(CPT >= 1, "tile too small for the workgroup");
+    static_assert(BM / 2 <= 64, "statistics DMA covers at most 64 chunks");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * STAGE];
     lds_u8* const smem = (lds_u8*)smem_raw;
@@ -357,6 +370,14 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         const int row = s / NCH, phys = s % NCH;
         toff[i] = (row * D + (phys ^ dswz<D>(row)) * 8) * 2;
     }
+    // Statistics DMA (wave 0): lanes 0 .. BM/4-1 fetch the tile's LSE * log2(e) in 4-row chunks,
+    // lanes BM/4 .. BM/2-1 its Dr; the other lanes point past the buffer and write zeros.
+    const int plane = p.B * p.H * p.nq_pad;
+    const int stat_total = 2 * plane * 4;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc((void*)p.stats, 0, stat_total, kBufferWord3);
+    const int soff = lane < BM / 4 ? (bh * p.nq_pad + 4 * lane) * 4
+                     : lane < BM / 2 ? (plane + bh * p.nq_pad + 4 * (lane - BM / 4)) * 4
+                                     : stat_total;
     auto issue_tile = [&](const int tile, const int stage) {
         const int i0 = tile * BM;
         const int bytes = (p.Nq - i0) * D * 2;  // rows past Nq arrive as zeros
@@ -373,6 +394,11 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         for (int i = 0; i < CPT; ++i) {
             lds_u8* dd = smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)dd, 16, toff[i], 0, 0, 0);
+        }
+        if (wave == 0) {
+            lds_u8* sd = smem + stage * STAGE + 2 * TILE;
+            const int off = soff < stat_total ? soff + i0 * 4 : stat_total;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void*)sd, 16, off, 0, 0, 0);
         }
     };
 
@@ -402,9 +428,6 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         dva[t] = f32x16_t{};
     }
     const float c2 = p.scale_log2;
-    // this slice's rows of the two statistics planes (padded to whole 32-row tiles)
-    const float* lse2g = p.stats + (size_t)bh * p.nq_pad;
-    const float* drg = lse2g + (size_t)p.B * p.H * p.nq_pad;
 
     auto do_tile = [&](const int it, const int stage) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -416,50 +439,70 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         if (!wave_has_keys || (p.causal && i0 + BM - 1 < kw0)) return;
         const lds_u8* qb = smem + stage * STAGE;
         const lds_u8* db = qb + TILE;
+        const lds_u8* sb = qb + 2 * TILE;
 
-        // Row statistics of the tile: register i of the accumulators holds query
-        // i0 + 16 (i/8) + 8 g + i%8, so a lane needs rows i0 + 8 g + 0..7 and i0 + 16 + 8 g + 0..7.
-        f32x4_t ls[4], rs[4];
+        // S = Q K^T and dP = dO V^T, 32 queries x 32 keys per block
+        f32x16_t s[QB], dp[QB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int qb2 = 0; qb2 < QB; ++qb2) {
+            s[qb2] = f32x16_t{};
+            dp[qb2] = f32x16_t{};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int row = i0 + 16 * h + 8 * g + 4 * u;  // < nq_pad: i0 + 32 <= nq_pad
-                ls[2 * h + u] = *(const f32x4_t*)(lse2g + row);
-                rs[2 * h + u] = *(const f32x4_t*)(drg + row);
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const u32x4_t a = *(const lds_u32x4*)(qb + raddr[ks] + qb2 * 32 * RB);
+                s[qb2] = M::mma(__builtin_bit_cast(vec8, a), kf[ks], s[qb2]);
             }
-
-        // S = Q K^T and dP = dO V^T (32 queries x 32 keys of this wave)
-        f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const u32x4_t a = *(const lds_u32x4*)(qb + raddr[ks]);
-            s = M::mma(__builtin_bit_cast(vec8, a), kf[ks], s);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const u32x4_t a = *(const lds_u32x4*)(db + raddr[ks]);
-            dp = M::mma(__builtin_bit_cast(vec8, a), vf[ks], dp);
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const u32x4_t a = *(const lds_u32x4*)(db + raddr[ks] + qb2 * 32 * RB);
+                dp[qb2] = M::mma(__builtin_bit_cast(vec8, a), vf[ks], dp[qb2]);
+            }
         }
 
-        // Rows past Nq carry an LSE of +inf, so their weights are already 0.
+        // Register i of s[qb2] holds query i0 + 32 qb2 + 16 (i/8) + 8 g + i%8.  Rows past Nq carry
+        // an LSE of +inf, so their weights are already 0.  Tile row of registers 4 v .. 4 v + 3:
+        // 32 qb2 + 16 (v/2) + 8 g + 4 (v%2).
+        f32x4_t ls[QB][4], rs[QB][4];
+#pragma unroll
+        for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const int rl = 32 * qb2 + 16 * (v4 >> 1) + 8 * g + 4 * (v4 & 1);
+                ls[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + rl * 4);
+                rs[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + BM * 4 + rl * 4);
+            }
+        // the mask matters only if some key of the wave is padding or lies after some row
         const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0);
-        vec8 pb[2], dsb[2];
+        if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float dr = rs[i >> 2][i & 3];
-            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -ls[i >> 2][i & 3]));
-            if (need_mask) {
-                const int qrow = i0 + 16 * (i >> 3) + 8 * g + (i & 7);
-                if (kj >= kv_valid || (p.causal && kj > qrow)) pv = 0.f;
-            }
-            pb[i >> 3][i & 7] = (T)pv;
-            dsb[i >> 3][i & 7] = (T)(pv * (dp[i] - dr));
+            for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int qrow = i0 + 32 * qb2 + 16 * (i >> 3) + 8 * g + (i & 7);
+                    const bool off = kj >= kv_valid || (p.causal && kj > qrow);
+                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb2][i], c2, -ls[qb2][i >> 2][i & 3]));
+                    s[qb2][i] = off ? 0.f : pv;
+                }
+        } else {
+#pragma unroll
+            for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[qb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb2][i], c2, -ls[qb2][i >> 2][i & 3]));
         }
+        // P and dS = P (dP - Dr), rounded to T for the MFMAs
+        vec8 pb[2 * QB], dsb[2 * QB];
+#pragma unroll
+        for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                pb[2 * qb2 + (i >> 3)][i & 7] = (T)s[qb2][i];
+                dsb[2 * qb2 + (i >> 3)][i & 7] = (T)(s[qb2][i] * (dp[qb2][i] - rs[qb2][i >> 2][i & 3]));
+            }
 
         // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
 #pragma unroll
-        for (int h16 = 0; h16 < 2; ++h16) {
+        for (int h16 = 0; h16 < 2 * QB; ++h16) {
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
                 const s16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_lo[t] + 16 * h16 * RB));
