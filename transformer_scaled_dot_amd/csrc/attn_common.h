@@ -46,8 +46,9 @@ __device__ __forceinline__ BlockWork block_work(const Params& p, int blk) {
     return w;
 }
 
-// Keys [lo, hi) that row i may attend to, before the padding length: the causal rule keeps
-// j <= i, the local band keeps |i - j| <= w.
+// Keys [lo, hi) that row i may attend to, within the valid length: the causal rule keeps
+// j <= i (top-left), or j <= i + L_b - Nq when the queries are the last Nq positions of a
+// cached sequence of length L_b (bottom-right); the local band keeps |i - j| <= w.
 __device__ __forceinline__ int row_key_lo(const Params& p, int i) {
     return p.window >= 0 ? i - p.window : 0;
 }

@@ -4,7 +4,8 @@
 // softmax, never store S), but on the vector ALUs: fp32 MFMA would change nothing in the
 // precision and this path serves small fp32 problems.  One wave per workgroup, one query row
 // per lane; K and V rows are read from LDS as broadcasts, the Q tile sits in LDS with a padded
-// row stride so that the 64 lanes reading one column hit 64 different banks.
+// row stride so that the 64 lanes reading one column hit 64 different banks.  The same key
+// splits as the matrix-core kernel apply (partial results for the merge kernel).
 #include "attn_common.h"
 
 namespace {

@@ -24,7 +24,10 @@
 //     ln 2 (m + log2 l) unchanged;
 //   * tiles outside every row's visible keys are never loaded (causal, key padding and the
 //     local band |i - j| <= w of sliding-window attention, lshu.cn page sec.2); masks are
-//     evaluated only on the tiles that straddle a boundary.
+//     evaluated only on the tiles that straddle a boundary;
+//   * for queries at the end of a KV cache the keys of a Q tile may be split over several
+//     workgroups (hotelren.com page sec.3.1); each then writes its fp32 partial O and LSE for the
+//     log-sum-exp merge instead of the final output.
 #include "attn_common.h"
 
 namespace {
