@@ -106,3 +106,29 @@ def test_backward_graph_replays():
 
     replays(cap, eager, [q, k, v, do])
     assert np.isfinite(dq.float().cpu().numpy()).all()
+
+
+def test_concurrent_streams_match_sequential():
+    """The library keeps no state: calls on two streams at once (default priority) give the same
+    bits as the same calls one after the other."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    mk = lambda *s: torch.randn(*s, device="cuda", generator=g).to(torch.bfloat16)
+    q1, k1, v1 = mk(2, 8, 700, 128), mk(2, 8, 700, 128), mk(2, 8, 700, 128)
+    q2, k2, v2 = mk(1, 4, 1, 128), mk(1, 4, 9000, 128), mk(1, 4, 9000, 128)
+    ref1 = binding.fwd(q1, k1, v1, causal=True)
+    ref2 = binding.decode(q2, k2, v2, causal=True)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = binding.fwd(q1, k1, v1, causal=True, stream=s1)
+        with torch.cuda.stream(s2):
+            b = binding.decode(q2, k2, v2, causal=True, stream=s2)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in outs:
+        assert torch.equal(a[0], ref1[0]) and torch.equal(a[1], ref1[1])
+        assert torch.equal(b[0], ref2[0]) and torch.equal(b[1], ref2[1])
