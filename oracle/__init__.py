@@ -48,8 +48,8 @@ class Oracle:
         lib.oracle_attn_bwd.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-            ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.oracle_decode.restype = ctypes.c_double
         lib.oracle_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]
@@ -108,14 +108,15 @@ class Oracle:
         return o.reshape(B, H, Nq, D), lse.reshape(B, H, Nq)
 
     def attn_bwd(self, q, k, v, do, dtype: str, scale, causal: bool = False, key_lens=None,
-                 dlse=None, bh=None, nthreads: int = 0):
+                 dlse=None, bh=None, nthreads: int = 0, window=None):
         """Reference gradients dQ, dK, dV (fp64) of the attention forward.
 
         q, do: [B,H,Nq,D]; k, v: [B,H,Nk,D] in storage form (bf16 as uint16 bits); do is the
         gradient of the loss with respect to O.  dlse: float32 [B,H,Nq] gradient with respect
         to the LSE output, or None (zero).  causal: False/True (top-left).  bh: slice ids
-        b*H + h to compute, or None for all.  Returns dq [n,Nq,D], dk [n,Nk,D], dv [n,Nk,D]
-        for the n selected slices, reshaped to [B,H,...] when bh is None.
+        b*H + h to compute, or None for all.  window=w keeps only keys with |i - j| <= w (None:
+        no band).  Returns dq [n,Nq,D], dk [n,Nk,D], dv [n,Nk,D] for the n selected slices,
+        reshaped to [B,H,...] when bh is None.
         """
         q = _as_storage(q, dtype)
         k = _as_storage(k, dtype)
@@ -138,8 +139,11 @@ class Oracle:
         dq = np.empty((n, Nq, D), np.float64)
         dk = np.empty((n, Nk, D), np.float64)
         dv = np.empty((n, Nk, D), np.float64)
+        w = -1 if window is None else int(window)
+        if w < -1:
+            raise ValueError("window must be None or >= 0")
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(g), _CODES[dtype],
-                                      B, H, Nq, Nk, D, float(scale), int(causal), _ptr(kl),
+                                      B, H, Nq, Nk, D, float(scale), int(causal), w, _ptr(kl),
                                       _ptr(sel), n, _ptr(dq), _ptr(dk), _ptr(dv), int(nthreads))
         if rc != 0:
             raise ValueError(f"oracle_attn_bwd failed with {rc}")

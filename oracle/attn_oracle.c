@@ -208,7 +208,8 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int
 }
 
 /*
- * Backward pass (gradients of the forward above, for causal in {0, 1} and no window).
+ * Backward pass (gradients of the forward above, for causal in {0, 1}, with or without a
+ * local band).
  *
  * With the row probabilities P[i,j] = e_j / l over J(i) (0 outside it) and a scalar loss whose
  * gradients with respect to the outputs are dO (same shape as O) and dlse (same shape as lse,
@@ -232,29 +233,36 @@ int oracle_attn_rows(const void* q, const void* k, const void* v, int dtype, int
  * key's sums can be formed independently.
  */
 typedef struct {
-    int dtype, Nq, Nk, D, causal;
+    int dtype, Nq, Nk, D, causal, window;
     double scale;
 } bwd_shape;
 
-/* keys [0, jend) visible to row i of a batch with L valid keys (causal 0 / 1) */
+/* keys [bwd_jbeg, bwd_jend) visible to row i of a batch with L valid keys: causal 0 / 1, and
+ * the band |i - j| <= window when window >= 0 */
+static int64_t bwd_jbeg(const bwd_shape* sh, int i) {
+    return sh->window >= 0 && (int64_t)i - sh->window > 0 ? (int64_t)i - sh->window : 0;
+}
 static int64_t bwd_jend(const bwd_shape* sh, int64_t L, int i) {
     int64_t jend = L;
     if (sh->causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;
+    if (sh->window >= 0 && jend > (int64_t)i + sh->window + 1) jend = (int64_t)i + sh->window + 1;
     return jend;
 }
 
 /*
  * oracle_attn_bwd -- reference gradients for selected (b, h) slices.
  *   q, dO: [B,H,Nq,D]; k, v: [B,H,Nk,D]; contiguous, stored as `dtype`.
- *   dlse: fp32 [B,H,Nq] or NULL (zero).  causal: 0 or 1.  key_lens: int32[B] or NULL.
+ *   dlse: fp32 [B,H,Nq] or NULL (zero).  causal: 0 or 1.  window: half-width of the local band
+ *   |i - j| <= window, or any negative value for none.  key_lens: int32[B] or NULL.
  *   bh: slice ids b*H + h (n_bh of them), or NULL for all B*H in order.
  *   dq: fp64 [n_bh, Nq, D]; dk, dv: fp64 [n_bh, Nk, D].
  * Returns 0, -1 on a bad argument, -2 if memory cannot be allocated.
  */
 int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
                     const float* dlse, int dtype, int B, int H, int Nq, int Nk, int D,
-                    double scale, int causal, const int32_t* key_lens, const int64_t* bh,
-                    int64_t n_bh, double* dq, double* dk, double* dv, int nthreads) {
+                    double scale, int causal, int window, const int32_t* key_lens,
+                    const int64_t* bh, int64_t n_bh, double* dq, double* dk, double* dv,
+                    int nthreads) {
     if (!q || !k || !v || !dO || !dq || !dk || !dv) return -1;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return -1;
     if (dtype != OR_F32 && dtype != OR_F16 && dtype != OR_BF16) return -1;
@@ -267,7 +275,7 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
     nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #endif
     (void)nthreads;
-    const bwd_shape sh = {dtype, Nq, Nk, D, causal, scale};
+    const bwd_shape sh = {dtype, Nq, Nk, D, causal, window < 0 ? -1 : window, scale};
     /* one slice at a time: its inputs widened to fp64, lse and Dr per row */
     const size_t nq = (size_t)Nq * D, nk = (size_t)Nk * D;
     double* buf = (double*)malloc(sizeof(double) * (2 * nq + 2 * nk + 2 * (size_t)Nq));
@@ -313,27 +321,27 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
             const double* gi = dOd + (size_t)i * D;
             double* dqi = dqs + (size_t)i * D;
             for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-            const int64_t n = bwd_jend(&sh, L, i);
-            if (n <= 0) {
+            const int64_t jb = bwd_jbeg(&sh, i), n = bwd_jend(&sh, L, i);
+            if (n <= jb) {
                 lse[i] = -INFINITY;
                 Dr[i] = 0.0;
                 continue;
             }
-            /* logits, max, sum, probabilities */
+            /* logits, max, sum, probabilities (P[j], dP[j] hold key j) */
             double m = -INFINITY;
-            for (int64_t j = 0; j < n; ++j) {
+            for (int64_t j = jb; j < n; ++j) {
                 double acc = 0.0;
                 for (int d = 0; d < D; ++d) acc += qi[d] * Kd[j * D + d];
                 P[j] = sh.scale * acc;
                 if (P[j] > m) m = P[j];
             }
             double l = 0.0;
-            for (int64_t j = 0; j < n; ++j) l += exp(P[j] - m);
+            for (int64_t j = jb; j < n; ++j) l += exp(P[j] - m);
             lse[i] = m + log(l);
-            for (int64_t j = 0; j < n; ++j) P[j] = exp(P[j] - m) / l;
+            for (int64_t j = jb; j < n; ++j) P[j] = exp(P[j] - m) / l;
             /* dP and Dr = sum_j P dP */
             double Dsum = 0.0;
-            for (int64_t j = 0; j < n; ++j) {
+            for (int64_t j = jb; j < n; ++j) {
                 double acc = 0.0;
                 for (int d = 0; d < D; ++d) acc += gi[d] * Vd[j * D + d];
                 dP[j] = acc;
@@ -342,7 +350,7 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
             Dr[i] = Dsum;
             /* dq = scale sum_j P (dP - Dr + g) k_j */
             const double g = dlse ? (double)dlse[s_bh * Nq + i] : 0.0;
-            for (int64_t j = 0; j < n; ++j) {
+            for (int64_t j = jb; j < n; ++j) {
                 const double ds = P[j] * (dP[j] - Dsum + g);
                 for (int d = 0; d < D; ++d) dqi[d] += sh.scale * ds * Kd[j * D + d];
             }
@@ -356,7 +364,7 @@ int oracle_attn_bwd(const void* q, const void* k, const void* v, const void* dO,
             for (int d = 0; d < D; ++d) dkj[d] = dvj[d] = 0.0;
             if (j >= L) continue; /* padding keys are never seen */
             for (int i = 0; i < Nq; ++i) {
-                if ((int64_t)j >= bwd_jend(&sh, L, i)) continue;
+                if ((int64_t)j < bwd_jbeg(&sh, i) || (int64_t)j >= bwd_jend(&sh, L, i)) continue;
                 const double* qi = Qd + (size_t)i * D;
                 const double* gi = dOd + (size_t)i * D;
                 double acc = 0.0, dp = 0.0;

@@ -543,7 +543,7 @@ def pin_bwd_finite_differences(impl):
                         f"d/d{name} causal={causal} dlse={with_g}: fd {fd:.9e} vs {an:.9e}"
 
 
-def torch_grads_f64(q, k, v, do, dtype, scale, causal, key_lens, dlse=None):
+def torch_grads_f64(q, k, v, do, dtype, scale, causal, key_lens, dlse=None, window=None):
     """Gradients of sum(O * dO) + sum(lse * dlse) by torch autograd in float64 through the
     explicit masked softmax (True = may attend); rows with no valid key contribute nothing."""
     import torch
@@ -557,6 +557,8 @@ def torch_grads_f64(q, k, v, do, dtype, scale, causal, key_lens, dlse=None):
     allow = torch.ones(B, 1, Nq, Nk, dtype=torch.bool)
     if causal:
         allow &= (j <= i)[None, None]
+    if window is not None:
+        allow &= ((i - j).abs() <= window)[None, None]
     if key_lens is not None:
         allow &= (j[None] < torch.from_numpy(np.asarray(key_lens, np.int64))[:, None, None])[:, None]
     s = torch.matmul(qd, kd.transpose(-2, -1)) * float(scale)
@@ -693,6 +695,70 @@ def pin_bwd_invariants(impl):
     close(rk[2], dv[:, :, pk], 1e-13, "key permutation: dv")
 
 
+def pin_bwd_window(impl):
+    """Backward with a local band |i - j| <= w: torch autograd with the band mask; central
+    differences of the forward oracle's banded loss; w = 0 (each row sees only key i: dq = scale
+    g_i k_i, dk_i = scale g_i q_i, dv_i = dO_i, zero for keys whose row does not exist or is
+    padding); a band at least as wide as the sequence gives the unbanded gradients bit for bit."""
+    rng = np.random.default_rng(35)
+    for dtype in ("f32", "bf16"):
+        for causal in (False, True):
+            for w in (0, 2, 5):
+                B, H, Nq, Nk, D = 3, 2, 9, 11, 8
+                q, do = (rand_store(rng, (B, H, Nq, D), dtype) for _ in range(2))
+                k, v = (rand_store(rng, (B, H, Nk, D), dtype) for _ in range(2))
+                kl = np.array([11, 6, 0], np.int32)
+                g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+                got = impl.attn_bwd(q, k, v, do, dtype, 0.35, causal, kl, g, window=w)
+                want = torch_grads_f64(q, k, v, do, dtype, 0.35, causal, kl, g, window=w)
+                for n, a, b in zip(("dq", "dk", "dv"), got, want):
+                    close(a, b, 1e-12, f"band autograd {n} {dtype} causal={causal} w={w}")
+    # central differences with a band
+    B, H, Nq, Nk, D = 2, 2, 7, 9, 5
+    x = {n: rand_store(rng, (B, H, Nq if n == "q" else Nk, D), "f32") for n in "qkv"}
+    G = rand_store(rng, (B, H, Nq, D), "f32")
+    gl = rng.standard_normal((B, H, Nq)).astype(np.float32)
+    kl = np.array([9, 5], np.int32)
+    grads = dict(zip("qkv", impl.attn_bwd(x["q"], x["k"], x["v"], G, "f32", 0.4, True, kl, gl, window=2)))
+
+    def loss(xx):
+        o, lse = impl.attn_rows(xx["q"], xx["k"], xx["v"], "f32", 0.4, True, kl, window=2)
+        fin = np.isfinite(lse)
+        return float(np.sum(o * G.reshape(-1, D).astype(np.float64))) + \
+            float(np.sum((lse * gl.reshape(-1).astype(np.float64))[fin]))
+
+    for name in "qkv":
+        u = rng.standard_normal(x[name].shape) * 1e-3
+        xp, xm = dict(x), dict(x)
+        xp[name] = (x[name].astype(np.float64) + u).astype(np.float32)
+        xm[name] = (x[name].astype(np.float64) - u).astype(np.float32)
+        fd = loss(xp) - loss(xm)
+        an = float(np.sum(grads[name] * (xp[name].astype(np.float64) - xm[name].astype(np.float64))))
+        assert abs(fd - an) <= 1e-5 * max(abs(fd), 1e-3), f"band d/d{name}: fd {fd:.9e} vs {an:.9e}"
+    # w = 0
+    B, H, Nq, Nk, D = 2, 2, 6, 8, 4
+    q, do = (rand_store(rng, (B, H, Nq, D), "f32") for _ in range(2))
+    k, v = (rand_store(rng, (B, H, Nk, D), "f32") for _ in range(2))
+    g = rng.standard_normal((B, H, Nq)).astype(np.float32)
+    kl = np.array([8, 4], np.int32)
+    for causal in (False, True):
+        dq, dk, dv = impl.attn_bwd(q, k, v, do, "f32", 0.6, causal, kl, g, window=0)
+        wq, wk, wv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+        for b in range(B):
+            for i in range(min(Nq, int(kl[b]))):
+                wq[b, :, i] = 0.6 * g[b, :, i, None].astype(np.float64) * k[b, :, i]
+                wk[b, :, i] = 0.6 * g[b, :, i, None].astype(np.float64) * q[b, :, i]
+                wv[b, :, i] = do[b, :, i]
+        close(dq, wq, 1e-14, "w=0 dq")
+        close(dk, wk, 1e-14, "w=0 dk")
+        close(dv, wv, 0.0, "w=0 dv")
+    # a band at least as wide as the sequence
+    for causal in (False, True):
+        a = impl.attn_bwd(q, k, v, do, "f32", 0.6, causal, kl, g, window=Nk)
+        b = impl.attn_bwd(q, k, v, do, "f32", 0.6, causal, kl, g)
+        assert all(np.array_equal(x1, x2) for x1, x2 in zip(a, b)), "wide band = no band"
+
+
 ALL_PINS = [
     pin_zero_query_mean, pin_scale_zero, pin_causal_row0, pin_single_key, pin_two_keys,
     pin_one_hot_dominant, pin_huge_logit_gap, pin_empty_rows, pin_rows_sum_to_one,
@@ -700,4 +766,5 @@ ALL_PINS = [
     pin_torch_sdpa_window, pin_window_zero_query_mean, pin_window_extremes, pin_bottom_right_causal,
     pin_golden_bruteforce, pin_decoders,
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_closed_forms, pin_bwd_invariants,
+    pin_bwd_window,
 ]

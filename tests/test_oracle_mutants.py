@@ -56,10 +56,16 @@ MUTANTS = [
     ("bwd row term without P", "Dsum += P[j] * acc;", "Dsum += acc;"),
     ("bwd P not normalised", "P[j] = exp(P[j] - m) / l;", "P[j] = exp(P[j] - m);"),
     ("bwd lse without max", "lse[i] = m + log(l);", "lse[i] = log(l);"),
-    ("bwd causal ignored in key pass", "if ((int64_t)j >= bwd_jend(&sh, L, i)) continue;", ""),
+    ("bwd visibility ignored in key pass", "if ((int64_t)j < bwd_jbeg(&sh, i) || (int64_t)j >= bwd_jend(&sh, L, i)) continue;", ""),
     ("bwd causal off by one", "if (sh->causal && jend > (int64_t)i + 1) jend = (int64_t)i + 1;",
      "if (sh->causal && jend > (int64_t)i) jend = (int64_t)i;"),
     ("bwd dO decoded from Q", "dOd[x] = dec(dO, dtype, (int64_t)(s_bh * nq + x));", "dOd[x] = dec(q, dtype, (int64_t)(s_bh * nq + x));"),
+    ("bwd band start ignored (key pass)", "if ((int64_t)j < bwd_jbeg(&sh, i) || (int64_t)j >= bwd_jend(&sh, L, i)) continue;",
+     "if ((int64_t)j >= bwd_jend(&sh, L, i)) continue;"),
+    ("bwd band start ignored (row pass)", "const int64_t jb = bwd_jbeg(&sh, i), n = bwd_jend(&sh, L, i);",
+     "const int64_t jb = 0, n = bwd_jend(&sh, L, i);"),
+    ("bwd band end off by one", "if (sh->window >= 0 && jend > (int64_t)i + sh->window + 1) jend = (int64_t)i + sh->window + 1;",
+     "if (sh->window >= 0 && jend > (int64_t)i + sh->window) jend = (int64_t)i + sh->window;"),
     ("bwd key lengths ignored", "            L = key_lens[b];\n            if (L < 0) L = 0;\n            if (L > Nk) L = Nk;\n        }\n        for (size_t x",
      "            L = Nk;\n        }\n        for (size_t x"),
 ]
