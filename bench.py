@@ -92,12 +92,13 @@ def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
     order = rng.permutation(w.B * w.H)
     args = (x["q"], x["k"], x["v"], do, w.dtype, float(x["scale"]), w.causal, x["key_lens"])
     n, spent, done = 1, 0.0, []
+    wkw = {} if w.window is None else {"window": w.window}
     while True:
         sel = order[len(done):len(done) + n]
         if sel.size == 0:
             break
         t0 = time.perf_counter()
-        want = impl.attn_bwd(*args, None, sel)
+        want = impl.attn_bwd(*args, None, sel, **wkw)
         spent += time.perf_counter() - t0
         done.append((sel, want))
         if spent >= 0.5 * target_s:
@@ -108,8 +109,8 @@ def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
     pairs = 0
     for bh in slices:
         L = w.Nk if kl is None else int(np.clip(kl[bh // w.H], 0, w.Nk))
-        i = np.arange(w.Nq)
-        pairs += int(np.minimum(L, i + 1).sum()) if w.causal else w.Nq * L
+        pairs += int(row_pairs(w, np.arange(w.Nq, dtype=np.int64), None if kl is None else
+                               np.full(w.B, L, np.int32)).sum())
     flops = 2.5 * 4.0 * w.D * pairs
     errs = []
     for sel, want in done:
@@ -274,21 +275,23 @@ def main():
     lib = binding.load_library()
     bwd = a.which == "bwd"
     if bwd:
-        if w.kv_cache or w.window is not None or w.dtype == "f32":
-            raise SystemExit(f"bench.py: the backward takes bf16/fp16 workloads without a window or KV cache ({name})")
-        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream)
+        if w.kv_cache or w.dtype == "f32":
+            raise SystemExit(f"bench.py: the backward takes bf16/fp16 workloads without a KV cache ({name})")
+        binding.fwd(q, k, v, causal=w.causal, key_lens=kl, scale=scale, out=o, lse=lse, stream=stream,
+                    window=w.window)
         do_np = inputs.make_grad_out(w)
         do = to_dev(do_np)
         grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
         ws_bytes = binding.attn_bwd_workspace_size(w.B, w.H, w.Nq)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         binding.bwd(q, k, v, o, lse, do, causal=w.causal, key_lens=kl, scale=scale, dq=grads[0],
-                    dk=grads[1], dv=grads[2], workspace=workspace, stream=stream)
+                    dk=grads[1], dv=grads[2], workspace=workspace, stream=stream, window=w.window)
+        win = -1 if w.window is None else min(int(w.window), 2**31 - 1)
         args = (*ptrs[:4], do.data_ptr(), lse.data_ptr(), None, *(t.data_ptr() for t in grads), *dims,
-                kl_ptr, code, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
+                win, kl_ptr, code, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
 
         def step():
-            rc = lib.attn_bwd(*args)
+            rc = lib.attn_bwd_window(*args)
             if rc != binding.ATTN_OK:
                 raise binding.AttnError(rc)
     elif w.kv_cache:

@@ -49,6 +49,20 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attn_bwd_window -- attn_bwd for the forward of attn_fwd_window: the gradients of attention
+ * restricted to the local band |i - j| <= window (on top of the causal and padding rules).
+ * window -1 is no band (identical to attn_bwd); a band at least max(Nq, Nk) wide is no band;
+ * window < -1 returns ATTN_ERR_WINDOW and writes nothing.  o and lse must come from
+ * attn_fwd_window with the same window.  Key and query tiles outside every band are skipped.
+ * Other arguments, layout, workspace, ownership and errors as attn_bwd.
+ */
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
+                    int Nq, int Nk, int D, float scale, int causal, int window,
+                    const int32_t* key_lens, int dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Workspace bytes attn_bwd needs: 2 * B * H * round_up(Nq, 64) * 4; 0 for B, H or Nq < 1.
  * attn_bwd returns ATTN_ERR_SHAPE when this exceeds 2^31 - 1 bytes. */
 size_t attn_bwd_workspace_size(int B, int H, int Nq);

@@ -169,3 +169,18 @@ def test_bwd_workspace_size():
     assert ws(1, 1, 65) == 2 * 128 * 4
     assert ws(1, 32, 16384) == 2 * 32 * 16384 * 4
     assert ws(0, 1, 1) == 0 and ws(1, 0, 1) == 0 and ws(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(window=-2), -9), (dict(window=-1000), -9), (dict(q=None), -1), (dict(dtype=0), -4),
+    (dict(causal=2), -6), (dict(ws=None), -1),
+])
+def test_host_validation_bwd_window(over, code):
+    """attn_bwd_window checks its band argument on the host like the others."""
+    a = dict(BWD_OK, window=16)
+    a.update(over)
+    rc = binding.attn_bwd_window(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dlse"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"], a["scale"],
+                                 a["causal"], a["window"], a["key_lens"], a["dtype"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+    assert rc == code

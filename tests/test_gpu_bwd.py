@@ -4,8 +4,9 @@ The forward runs on the GPU (attn_fwd) to produce the O and LSE the backward tak
 expected gradients come from oracle.attn_bwd on the same stored inputs.  Tolerance, per
 gradient tensor: max |GPU - oracle| <= 2e-2 * max |oracle| for bf16 / fp16 (the forward's bf16
 bound applied to the gradient scaled to unit size: P and dS are rounded to the input type
-before their products, a relative error of about 2^-9 per term); gradient rows that are zero by
-structure (keys no row may see, rows of a batch with no valid key) must be exactly zero.
+before their products, a relative error of about 2^-9 per term), with max |oracle| taken at least
+1e-3; gradient rows that are zero by structure (keys no row may see, rows that see no key) must
+be exactly zero.
 """
 import numpy as np
 import pytest
@@ -17,33 +18,46 @@ from transformer_scaled_dot_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 TOL_G = 2e-2
+# A gradient that is zero only by exact cancellation (one visible key per row: dP = Dr) keeps an
+# fp32 residue of about 1e-6 on the GPU, where dP comes from the MFMA and Dr from the rounded O;
+# the bound never drops below TOL_G * FLOOR_G = 2e-5.
+FLOOR_G = 1e-3
 
 
 def log(msg):
     print(msg, flush=True)
 
 
-def run_fwd_bwd(x, dtype, causal, dlse=None, scale=None):
+def run_fwd_bwd(x, dtype, causal, dlse=None, scale=None, window=None):
     """GPU forward then backward on stored inputs x (q, k, v, do, key_lens, scale)."""
     q, k, v, do = (to_device(x[n], dtype) for n in ("q", "k", "v", "do"))
     kl = None if x.get("key_lens") is None else torch.from_numpy(np.asarray(x["key_lens"], np.int32)).cuda()
     s = float(x["scale"]) if scale is None else float(scale)
-    o, lse = binding.fwd(q, k, v, causal=causal, key_lens=kl, scale=s)
+    o, lse = binding.fwd(q, k, v, causal=causal, key_lens=kl, scale=s, window=window)
     g = None if dlse is None else torch.from_numpy(np.asarray(dlse, np.float32)).cuda()
-    dq, dk, dv = binding.bwd(q, k, v, o, lse, do, causal=causal, key_lens=kl, scale=s, dlse=g)
+    dq, dk, dv = binding.bwd(q, k, v, o, lse, do, causal=causal, key_lens=kl, scale=s, dlse=g, window=window)
     torch.cuda.synchronize()
     return dq, dk, dv
 
 
-def unseen(x, causal, H, bh=None):
-    """Masks of gradient rows that are zero by structure: dq rows of a batch with no valid key,
-    dk / dv rows of keys that no query row may see."""
+def unseen(x, causal, H, bh=None, window=None):
+    """Masks of gradient rows that are zero by structure: dq rows that see no valid key, dk / dv
+    rows of keys that no query row may see."""
     B, _, Nq, _ = x["q"].shape
     Nk = x["k"].shape[2]
     kl = np.full(B, Nk) if x.get("key_lens") is None else np.clip(np.asarray(x["key_lens"]), 0, Nk)
-    rows = np.repeat(kl == 0, H)[:, None] & np.ones((1, Nq), bool)          # [B*H, Nq]
+    i = np.arange(Nq)[None, :]
     j = np.arange(Nk)[None, :]
-    keys = (j >= np.repeat(kl, H)[:, None]) | ((j > Nq - 1) if causal else False)  # [B*H, Nk]
+    L = np.repeat(kl, H)[:, None]
+    lo = np.maximum(i - window, 0) if window is not None else np.zeros_like(i)
+    hi = np.minimum(L, i + 1) if causal else np.broadcast_to(L, (L.shape[0], Nq))
+    if window is not None:
+        hi = np.minimum(hi, i + window + 1)
+    rows = hi <= lo                                                            # [B*H, Nq]
+    first = np.maximum(j - window, 0) if window is not None else np.zeros_like(j)
+    if causal:
+        first = np.maximum(first, j)
+    keys = (j >= L) | (first > Nq - 1)                                         # [B*H, Nk]
     if bh is not None:
         rows, keys = rows[bh], keys[bh]
     return rows, keys
@@ -61,7 +75,7 @@ def compare_grads(got, want, what, bh=None, zero_rows=None):
             assert np.all(a[z] == 0.0) and np.all(b[z] == 0.0), f"{what} {name}: rows that must be zero"
         scale = float(np.max(np.abs(b))) if b.size else 0.0
         err = float(np.max(np.abs(a - b))) if b.size else 0.0
-        assert err <= TOL_G * max(scale, 1e-30), f"{what} {name}: max err {err:.3e} vs max |ref| {scale:.3e}"
+        assert err <= TOL_G * max(scale, FLOOR_G), f"{what} {name}: max err {err:.3e} vs max |ref| {scale:.3e}"
         log(f"[bwd] {what} {name}: max err {err:.3e} (max |ref| {scale:.3e}, ratio {err / max(scale, 1e-30):.2e})")
 
 
@@ -101,6 +115,53 @@ def test_bwd_parity(shape, dtype, oracle_impl):
                                         x["key_lens"], g)
             compare_grads(got, want, f"{name}/{dtype}/causal={causal}/dlse={with_g}",
                           zero_rows=unseen(x, causal, H))
+
+
+WIN_SHAPES = [
+    ("n300_d128", 2, 3, 300, 300, 128, None),
+    ("nq130_nk257_d64", 2, 2, 130, 257, 64, None),
+    ("padded_n200_d64", 4, 2, 200, 200, 64, [200, 150, 9, 0]),
+    ("n517_d128", 1, 2, 517, 517, 128, None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", WIN_SHAPES, ids=[s[0] for s in WIN_SHAPES])
+def test_bwd_window_parity(shape, dtype, oracle_impl):
+    """Backward of sliding-window attention against the oracle, bands from 0 to wider than a tile."""
+    name, B, H, Nq, Nk, D, kl = shape
+    x = make(B, H, Nq, Nk, D, dtype, 56, kl)
+    rng = np.random.default_rng(57)
+    for causal in (False, True):
+        for w in (0, 1, 31, 64, 100, 255):
+            g = rng.standard_normal((B, H, Nq)).astype(np.float32) if w % 2 else None
+            log(f"[bwd] {name} {dtype} causal={causal} window={w}")
+            got = run_fwd_bwd(x, dtype, causal, g, window=w)
+            want = oracle_impl.attn_bwd(x["q"], x["k"], x["v"], x["do"], dtype, float(x["scale"]), causal,
+                                        x["key_lens"], g, window=w)
+            compare_grads(got, want, f"{name}/{dtype}/causal={causal}/w={w}",
+                          zero_rows=unseen(x, causal, H, window=w))
+
+
+def test_bwd_wide_window_is_no_window_bitwise():
+    x = make(2, 2, 333, 333, 128, "bf16", 58, [333, 100])
+    for causal in (False, True):
+        a = run_fwd_bwd(x, "bf16", causal)
+        for w in (333, 10 ** 6):
+            b = run_fwd_bwd(x, "bf16", causal, window=w)
+            assert all(torch.equal(t1, t2) for t1, t2 in zip(a, b)), w
+
+
+def test_bwd_window_full_size_slices(oracle_impl):
+    """The 4K decoder workload with a band of 512, whole (b, h) slices against the oracle."""
+    w = inputs.WORKLOADS["decoder_window512_causal_bf16_b4h32n4096d128"]
+    x = inputs.make_inputs(w)
+    x["do"] = inputs.make_grad_out(w)
+    got = run_fwd_bwd(x, w.dtype, w.causal, window=w.window)
+    bh = np.array([0, 77, 127])
+    want = oracle_impl.attn_bwd(x["q"], x["k"], x["v"], x["do"], w.dtype, float(x["scale"]), w.causal,
+                                x["key_lens"], None, bh, window=w.window)
+    compare_grads(got, want, "decoder window 512", bh=bh, zero_rows=unseen(x, w.causal, w.H, bh, w.window))
 
 
 @pytest.mark.parametrize("scale", [-0.1, 0.0, 0.3])

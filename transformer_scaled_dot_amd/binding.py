@@ -26,7 +26,7 @@ STATUS = {
     -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size",
-           "attn_bwd", "attn_bwd_workspace_size", "attn_status_str")
+           "attn_bwd", "attn_bwd_window", "attn_bwd_workspace_size", "attn_status_str")
 
 _lib = None
 
@@ -75,6 +75,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p,
     ]
+    lib.attn_bwd_window.restype = ctypes.c_int
+    lib.attn_bwd_window.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p,
+    ]
     lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -112,6 +120,14 @@ def attn_bwd(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale, ca
     """The C entry point of the backward (dQ, dK, dV from dO and the forward's O and LSE)."""
     return load_library().attn_bwd(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale,
                                    causal, key_lens, dtype, workspace, workspace_bytes, stream)
+
+
+def attn_bwd_window(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, window,
+                    key_lens, dtype, workspace, workspace_bytes, stream) -> int:
+    """The C entry point of the backward with a local band |i - j| <= window (-1: no band)."""
+    return load_library().attn_bwd_window(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D,
+                                          scale, causal, window, key_lens, dtype, workspace,
+                                          workspace_bytes, stream)
 
 
 def attn_bwd_workspace_size(B, H, Nq) -> int:
@@ -235,10 +251,12 @@ def fwd(q, k, v, *, causal: bool = False, key_lens=None, scale: float | None = N
 
 
 def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: float | None = None,
-        dlse=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+        dlse=None, dq=None, dk=None, dv=None, workspace=None, stream=None, window: int | None = None):
     """dQ, dK, dV of attention(q, k, v) for the gradient `dout` of O (and `dlse` of LSE, or None).
-    o and lse are the forward's outputs for the same q, k, v, causal, key_lens and scale.
+    o and lse are the forward's outputs for the same q, k, v, causal, key_lens, scale and window.
     Tensors as for fwd (bf16 or fp16); returns (dq, dk, dv) in q's dtype."""
+    if window is not None and (int(window) != window or window < 0):
+        raise ValueError("window must be None or an integer >= 0")
     torch = _torch()
     B, H, Nq, Nk, D, code, scale, kl_ptr, out, lse_t, handle = _check(q, k, v, key_lens, scale, o, lse,
                                                                        stream)
@@ -265,10 +283,11 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: fl
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA tensor on q's device")
-    rc = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                  None if dlse is None else dlse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(),
-                  outs[2].data_ptr(), B, H, Nq, Nk, D, scale, int(bool(causal)), kl_ptr, code,
-                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), handle)
+    rc = attn_bwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                         lse.data_ptr(), None if dlse is None else dlse.data_ptr(), outs[0].data_ptr(),
+                         outs[1].data_ptr(), outs[2].data_ptr(), B, H, Nq, Nk, D, scale, int(bool(causal)),
+                         -1 if window is None else min(int(window), 2**31 - 1), kl_ptr, code,
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), handle)
     if rc != ATTN_OK:
         raise AttnError(rc)
     return tuple(outs)

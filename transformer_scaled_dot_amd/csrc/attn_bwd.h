@@ -30,7 +30,31 @@ struct BwdParams {
     float scale_log2;    // max(|scale| * log2(e), 1e-30)
     int negate;          // scale < 0: the sign is moved onto Q (dQ kernel) or K (dK/dV kernel)
     int causal;
+    int window;          // half-width w of the local band |i - j| <= w, or -1 for none
 };
+
+// Keys [lo, hi) row i may attend to within the valid length kv_valid: the top-left causal rule
+// keeps j <= i, the local band (WIN) keeps |i - j| <= w.
+template <bool WIN>
+__device__ __forceinline__ int bwd_key_lo(const BwdParams& p, int i) { return WIN ? i - p.window : 0; }
+template <bool WIN>
+__device__ __forceinline__ int bwd_key_hi(const BwdParams& p, int i, int kv_valid) {
+    int hi = kv_valid;
+    if (p.causal) hi = min(hi, i + 1);
+    if (WIN) hi = min(hi, i + p.window + 1);
+    return hi;
+}
+// Rows [lo, hi) that may see key j (before the query length): the inverse of the rules above.
+template <bool WIN>
+__device__ __forceinline__ int bwd_row_lo(const BwdParams& p, int j) {
+    int lo = p.causal ? j : 0;
+    if (WIN) lo = max(lo, j - p.window);
+    return max(lo, 0);
+}
+template <bool WIN>
+__device__ __forceinline__ int bwd_row_hi(const BwdParams& p, int j) {
+    return WIN ? min(p.Nq, j + p.window + 1) : p.Nq;
+}
 
 }  // namespace attn
 

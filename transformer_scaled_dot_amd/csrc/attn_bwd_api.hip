@@ -18,16 +18,18 @@ extern "C" size_t attn_bwd_workspace_size(int B, int H, int Nq) {
     return (size_t)2 * B * H * (size_t)nq_padded(Nq) * sizeof(float);
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
-                        int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+extern "C" int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                               const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B,
+                               int H, int Nq, int Nk, int D, float scale, int causal, int window,
+                               const int32_t* key_lens, int dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+    if (window < -1) return ATTN_ERR_WINDOW;
     const uintptr_t ptrs = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
                            (uintptr_t)lse | (uintptr_t)dlse | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
     if ((ptrs & 15) != 0 || ((uintptr_t)key_lens & 3) != 0) return ATTN_ERR_ALIGN;
@@ -73,5 +75,15 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     p.scale_log2 = (float)fmax(fabs((double)scale) * 1.4426950408889634074, 1e-30);
     p.negate = scale < 0.f;
     p.causal = causal;
+    // |i - j| < max(Nq, Nk) always holds: a band at least that wide is no band
+    p.window = window >= (Nq > Nk ? Nq : Nk) ? -1 : window;
     return attn_launch_bwd_mfma(p, dtype, D, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
+                        int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return attn_bwd_window(q, k, v, o, dout, lse, dlse, dq, dk, dv, B, H, Nq, Nk, D, scale, causal, -1,
+                           key_lens, dtype, workspace, workspace_bytes, stream);
 }

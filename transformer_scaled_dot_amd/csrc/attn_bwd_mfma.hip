@@ -85,7 +85,7 @@ __device__ __forceinline__ u32x4_t load8(const void* base, int bytes, int off_by
 }
 
 // ------------------------------------------------------------------------------------ dQ
-template <typename T, int D>
+template <typename T, int D, bool WIN>
 __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using M = Mma<T>;
@@ -122,7 +122,9 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
 
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
     const int q_last = min(p.Nq, q0 + BMQ) - 1;
-    const int kv_end = p.causal ? min(kv_valid, q_last + 1) : kv_valid;
+    // key tiles [t_begin, n_tiles) hold every key some row of this workgroup may see
+    const int kv_end = min(kv_valid, attn::bwd_key_hi<WIN>(p, q_last, kv_valid));
+    const int t_begin = max(0, attn::bwd_key_lo<WIN>(p, q0)) / BN;
     const int n_tiles = (kv_end + BN - 1) / BN;
 
     const size_t qbase = (size_t)bh * p.Nq * D;
@@ -218,7 +220,8 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
         if (it + 1 < n_tiles) issue_tile(it + 1, stage ^ 1);
 
         const int j0 = it * BN;
-        if (!wave_has_rows || (p.causal && j0 > qw0 + 31)) return;
+        if (!wave_has_rows || j0 >= attn::bwd_key_hi<WIN>(p, qw0 + 31, kv_valid) || j0 + BN <= attn::bwd_key_lo<WIN>(p, qw0))
+            return;
         const lds_u8* kb = smem + stage * STAGE;
         const lds_u8* vb = kb + TILE;
 
@@ -241,14 +244,15 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
 
         // Register i of s[kt] / dp[kt] holds key j0 + 32 kt + 16 (i/8) + 8 g + i%8.  The mask
         // matters only on tiles that reach past the valid keys or the wave's first row.
-        const bool need_mask = j0 + BN > kv_valid || (p.causal && j0 + BN - 1 > qw0);
+        const bool need_mask = j0 + BN > attn::bwd_key_hi<WIN>(p, qw0, kv_valid) || j0 < attn::bwd_key_lo<WIN>(p, qw0 + 31);
         if (need_mask) {
+            const int lo = attn::bwd_key_lo<WIN>(p, qi), hi = attn::bwd_key_hi<WIN>(p, qi, kv_valid);
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const bool off = j >= kv_valid || (p.causal && j > qi);
+                    const bool off = j < lo || j >= hi;
                     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], c2, -lse2));
                     s[kt][i] = off ? 0.f : pv;
                 }
@@ -280,8 +284,8 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
         }
     };
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int it = 0; it < n_tiles; it += 2) {
+    if (t_begin < n_tiles) issue_tile(t_begin, 0);
+    for (int it = t_begin; it < n_tiles; it += 2) {
         do_tile(it, 0);
         if (it + 1 < n_tiles) do_tile(it + 1, 1);
     }
@@ -306,7 +310,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------- dK, dV
-template <typename T, int D>
+template <typename T, int D, bool WIN>
 __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using M = Mma<T>;
@@ -348,9 +352,12 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
     const T* dog = (const T*)p.dout + qbase;
 
     // Query tiles [t_begin, n_tiles) hold every row that may see a key of this workgroup.
-    const int n_tiles = k0 < kv_valid ? (p.Nq + BM - 1) / BM : 0;
-    const int t_begin = p.causal ? min(k0, p.Nq) / BM : 0;
+    const int k_last = min(kv_valid, k0 + BNK) - 1;
+    const int n_tiles = k0 < kv_valid ? (attn::bwd_row_hi<WIN>(p, k_last) + BM - 1) / BM : 0;
+    const int t_begin = min(attn::bwd_row_lo<WIN>(p, k0), p.Nq) / BM;
     const bool wave_has_keys = kw0 < kv_valid;
+    const int wave_row_lo = attn::bwd_row_lo<WIN>(p, kw0);
+    const int wave_row_hi = attn::bwd_row_hi<WIN>(p, min(kw0 + 31, kv_valid - 1));
 
     // K^T and V^T operands: lane (r, g) holds key kj, columns 16 ks + 8 g .. +7.
     vec8 kf[KSTEPS], vf[KSTEPS];
@@ -436,7 +443,7 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
 
         const int i0 = it * BM;
         // nothing of this tile reaches the wave's keys
-        if (!wave_has_keys || (p.causal && i0 + BM - 1 < kw0)) return;
+        if (!wave_has_keys || i0 + BM <= wave_row_lo || i0 >= wave_row_hi) return;
         const lds_u8* qb = smem + stage * STAGE;
         const lds_u8* db = qb + TILE;
         const lds_u8* sb = qb + 2 * TILE;
@@ -472,14 +479,16 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
                 rs[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + BM * 4 + rl * 4);
             }
         // the mask matters only if some key of the wave is padding or lies after some row
-        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0);
+        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0) ||
+                               (WIN && (i0 + BM - 1 - kw0 > p.window || kw0 + 31 - i0 > p.window));
         if (need_mask) {
 #pragma unroll
             for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int qrow = i0 + 32 * qb2 + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const bool off = kj >= kv_valid || (p.causal && kj > qrow);
+                    const bool off = kj >= kv_valid || kj < attn::bwd_key_lo<WIN>(p, qrow) ||
+                                     kj >= attn::bwd_key_hi<WIN>(p, qrow, kv_valid);
                     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb2][i], c2, -ls[qb2][i >> 2][i & 3]));
                     s[qb2][i] = off ? 0.f : pv;
                 }
@@ -554,15 +563,21 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int D>
-hipError_t launch_one(const attn::BwdParams& p, hipStream_t stream) {
+template <typename T, int D, bool WIN>
+hipError_t launch_two(const attn::BwdParams& p, hipStream_t stream) {
     attn::BwdParams pc = p;
     void* args[] = {&pc};
-    hipError_t e = hipLaunchKernel((const void*)attn_bwd_dq_kernel<T, D>, dim3(p.n_blocks_q), dim3(NT),
+    hipError_t e = hipLaunchKernel((const void*)attn_bwd_dq_kernel<T, D, WIN>, dim3(p.n_blocks_q), dim3(NT),
                                    args, 0, stream);
     if (e != hipSuccess) return e;
-    return hipLaunchKernel((const void*)attn_bwd_dkdv_kernel<T, D>, dim3(p.n_blocks_k), dim3(NT), args,
+    return hipLaunchKernel((const void*)attn_bwd_dkdv_kernel<T, D, WIN>, dim3(p.n_blocks_k), dim3(NT), args,
                            0, stream);
+}
+
+// The band logic is compiled only into the windowed kernels.
+template <typename T, int D>
+hipError_t launch_one(const attn::BwdParams& p, hipStream_t stream) {
+    return p.window >= 0 ? launch_two<T, D, true>(p, stream) : launch_two<T, D, false>(p, stream);
 }
 
 }  // namespace
