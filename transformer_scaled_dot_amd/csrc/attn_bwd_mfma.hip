@@ -448,39 +448,39 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         const lds_u8* db = qb + TILE;
         const lds_u8* sb = qb + 2 * TILE;
 
-        // S = Q K^T and dP = dO V^T, 32 queries x 32 keys per block
-        f32x16_t s[QB], dp[QB];
+        // S = Q K^T, 32 queries x 32 keys per block.  Every row operand of S and dP is requested
+        // before the first product, so one wave per SIMD does not wait out the LDS latency per step.
+        static_assert(QB == 1, "one 32-row block per streamed tile");
+        u32x4_t qa[KSTEPS], da[KSTEPS];
 #pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2) {
-            s[qb2] = f32x16_t{};
-            dp[qb2] = f32x16_t{};
+        for (int ks = 0; ks < KSTEPS; ++ks) qa[ks] = *(const lds_u32x4*)(qb + raddr[ks]);
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const u32x4_t a = *(const lds_u32x4*)(qb + raddr[ks] + qb2 * 32 * RB);
-                s[qb2] = M::mma(__builtin_bit_cast(vec8, a), kf[ks], s[qb2]);
-            }
+        for (int ks = 0; ks < KSTEPS; ++ks) da[ks] = *(const lds_u32x4*)(db + raddr[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t s[QB];
+        s[0] = f32x16_t{};
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const u32x4_t a = *(const lds_u32x4*)(db + raddr[ks] + qb2 * 32 * RB);
-                dp[qb2] = M::mma(__builtin_bit_cast(vec8, a), vf[ks], dp[qb2]);
-            }
-        }
+        for (int ks = 0; ks < KSTEPS; ++ks) s[0] = M::mma(__builtin_bit_cast(vec8, qa[ks]), kf[ks], s[0]);
 
-        // Register i of s[qb2] holds query i0 + 32 qb2 + 16 (i/8) + 8 g + i%8.  Rows past Nq carry
-        // an LSE of +inf, so their weights are already 0.  Tile row of registers 4 v .. 4 v + 3:
-        // 32 qb2 + 16 (v/2) + 8 g + 4 (v%2).
-        f32x4_t ls[QB][4], rs[QB][4];
+        // Exponent of P in base 2: scale S log2(e) - LSE log2(e), or -inf where a row cannot see
+        // the key.  Register i of s[qb2] holds query i0 + 32 qb2 + 16 (i/8) + 8 g + i%8; rows
+        // past Nq carry an LSE of +inf, so their weights are already 0.  The statistics of tile
+        // rows 32 qb2 + 16 (v4/2) + 8 g + 4 (v4%2) + 0..3 sit in one 16-byte LDS read each.
+        f32x4_t rs[QB][4];
+        float x[QB][16];
+        // the mask matters only if some key of the wave is padding or lies outside some row's range
+        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0) ||
+                               (WIN && (i0 + BM - 1 - kw0 > p.window || kw0 + 31 - i0 > p.window));
 #pragma unroll
         for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int rl = 32 * qb2 + 16 * (v4 >> 1) + 8 * g + 4 * (v4 & 1);
-                ls[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + rl * 4);
+                const f32x4_t ls = *(const __attribute__((address_space(3))) f32x4_t*)(sb + rl * 4);
                 rs[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + BM * 4 + rl * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[qb2][4 * v4 + e] = __builtin_fmaf(s[qb2][4 * v4 + e], c2, -ls[e]);
             }
-        // the mask matters only if some key of the wave is padding or lies after some row
-        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0) ||
-                               (WIN && (i0 + BM - 1 - kw0 > p.window || kw0 + 31 - i0 > p.window));
         if (need_mask) {
 #pragma unroll
             for (int qb2 = 0; qb2 < QB; ++qb2)
@@ -489,24 +489,26 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
                     const int qrow = i0 + 32 * qb2 + 16 * (i >> 3) + 8 * g + (i & 7);
                     const bool off = kj >= kv_valid || kj < attn::bwd_key_lo<WIN>(p, qrow) ||
                                      kj >= attn::bwd_key_hi<WIN>(p, qrow, kv_valid);
-                    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb2][i], c2, -ls[qb2][i >> 2][i & 3]));
-                    s[qb2][i] = off ? 0.f : pv;
+                    x[qb2][i] = off ? -INFINITY : x[qb2][i];
                 }
-        } else {
-#pragma unroll
-            for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s[qb2][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb2][i], c2, -ls[qb2][i >> 2][i & 3]));
         }
-        // P and dS = P (dP - Dr), rounded to T for the MFMAs
+
+        // From here on one straight-line block (the mask above only edits x): dP = dO V^T runs on
+        // the matrix cores while the exponentials form P, and dS of the second 16 rows forms under
+        // the dV / dK products of the first 16.
+        f32x16_t dp[QB];
+        dp[0] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) dp[0] = M::mma(__builtin_bit_cast(vec8, da[ks]), vf[ks], dp[0]);
+        // P = 2^x and dS = P (dP - Dr), rounded to T for the MFMAs
         vec8 pb[2 * QB], dsb[2 * QB];
 #pragma unroll
         for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                pb[2 * qb2 + (i >> 3)][i & 7] = (T)s[qb2][i];
-                dsb[2 * qb2 + (i >> 3)][i & 7] = (T)(s[qb2][i] * (dp[qb2][i] - rs[qb2][i >> 2][i & 3]));
+                const float pv = __builtin_amdgcn_exp2f(x[qb2][i]);
+                pb[2 * qb2 + (i >> 3)][i & 7] = (T)pv;
+                dsb[2 * qb2 + (i >> 3)][i & 7] = (T)(pv * (dp[qb2][i] - rs[qb2][i >> 2][i & 3]));
             }
 
         // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
