@@ -2,40 +2,65 @@
 //
 // Same tiled loop as the matrix-core kernel (per Q tile, stream K/V tiles through LDS, online
 // softmax, never store S), but on the vector ALUs: fp32 MFMA would change nothing in the
-// precision and this path serves small fp32 problems.  One wave per workgroup, one query row
-// per lane; K and V rows are read from LDS as broadcasts, the Q tile sits in LDS with a padded
-// row stride so that the 64 lanes reading one column hit 64 different banks.  The same key
-// splits as the matrix-core kernel apply (partial results for the merge kernel).
+// precision and this path serves small fp32 problems.  One query row per lane; the NW waves of
+// a workgroup (eight for D = 64, four for D = 128) share the 64-row Q tile (in LDS, with a padded
+// row stride so that the 64 lanes reading one column hit 64 different banks) and split its keys,
+// wave w taking key tiles w, w + NW, ...  Each wave keeps its own running max, sum and output; at
+// the end the waves' partial states of a row are combined by the log-sum-exp rule (rescale each
+// to the common max, add the sums and the outputs), the same rule the split-K merge applies
+// across workgroups.  K and V rows are read from LDS as broadcasts.  The key splits of the
+// matrix-core kernel apply here too (partial results for the merge kernel).
 #include "attn_common.h"
 
 namespace {
 
 constexpr int BMF = 64;  // query rows per workgroup (one per lane)
+constexpr int BNF = 16;  // keys per K/V tile
+// waves per workgroup, each on every NW-th key tile (LDS: the Q tile plus one K and V tile per wave)
+template <int D>
+constexpr int waves_f32() { return D == 64 ? 8 : 4; }
+constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
-    constexpr int BNF = D == 128 ? 16 : 32;  // keys per K/V tile (keeps LDS under 64 KiB)
+__global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn::Params p) {
+    constexpr int NWF = waves_f32<D>();
     __shared__ float qs[BMF][D + 1];
-    __shared__ float ks[BNF][D];
-    __shared__ float vs[BNF][D];
+    __shared__ float kv[NWF][2][BNF][D];  // each wave's K and V tile; the merge reuses it
+    __shared__ float part_m[NWF][BMF], part_l[NWF][BMF];
+    static_assert(NWF * 2 * BNF * D >= BMF * (D + 1), "merge buffer does not fit");
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks));
     const int bh = bw.bh;
     int qt = bw.qt;
     if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;
     const int b = bh / p.H;
     const int q0 = qt * BMF;
-    const int qi = q0 + tid;
+    const int qi = q0 + lane;
 
     const float* qg = (const float*)p.q + (size_t)bh * p.Nq * D;
     const float* kg = (const float*)p.k + (size_t)bh * p.Nk * D;
     const float* vg = (const float*)p.v + (size_t)bh * p.Nk * D;
     const float qsign = p.negate_q ? -1.f : 1.f;
 
-    for (int idx = tid; idx < BMF * D; idx += BMF) {
-        const int row = idx / D, d = idx % D;
-        qs[row][d] = (q0 + row < p.Nq) ? qsign * qg[(size_t)(q0 + row) * D + d] : 0.f;
+    {
+        // 16-byte loads, all in flight together; rows past Nq fall outside the buffer and read as 0
+        constexpr int L4 = BMF * D / 4 / (BMF * NWF);
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(qg + (size_t)q0 * D), 0, (p.Nq - q0) * D * 4, kBufferWord3);
+        f32x4_t qx[L4];
+#pragma unroll
+        for (int i = 0; i < L4; ++i)
+            qx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, (i * BMF * NWF + tid) * 16, 0, 0));
+#pragma unroll
+        for (int i = 0; i < L4; ++i) {
+            const int e = (i * BMF * NWF + tid) * 4, row = e / D, d = e % D;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qs[row][d + c] = qsign * qx[i][c];
+        }
     }
 
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
@@ -46,34 +71,74 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
         kv_begin = max(kv_begin, bw.split * p.split_len);
         kv_end = min(kv_end, (bw.split + 1) * p.split_len);
     }
+    const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BNF - 1) / BNF : 0;
     const int lo = attn::row_key_lo(p, qi), hi = attn::row_key_hi(p, qi, kv_valid);
     const float c2 = p.scale_log2;
+    float (*const ks)[D] = kv[wave][0];
+    float (*const vs)[D] = kv[wave][1];
 
     float o[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int j0 = kv_begin; j0 < kv_end; j0 += BNF) {
+    // Round r: wave w takes tile r * NWF + w.  The barriers keep the waves in rounds, so a wave's
+    // tile loads never overtake another wave's reads of the Q tile or of its own previous tile.
+    for (int t0 = 0; t0 < n_tiles; t0 += NWF) {
+        const int t = t0 + wave;
+        const int j0 = kv_begin + t * BNF;
         __syncthreads();
-        for (int idx = tid; idx < BNF * D; idx += BMF) {
-            const int row = idx / D, d = idx % D;
-            const bool ok = j0 + row < kv_valid;
-            ks[row][d] = ok ? kg[(size_t)(j0 + row) * D + d] : 0.f;
-            vs[row][d] = ok ? vg[(size_t)(j0 + row) * D + d] : 0.f;
+        if (t < n_tiles) {
+            // 16-byte loads, all in flight together; rows at or past the valid length fall
+            // outside the buffer and read as zeros
+            constexpr int L4 = BNF * D / 4 / BMF;  // float4s per lane per tile
+            const int bytes = (kv_valid - j0) * D * 4;
+            const __amdgpu_buffer_rsrc_t krs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+            const __amdgpu_buffer_rsrc_t vrs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (size_t)j0 * D), 0, bytes, kBufferWord3);
+            f32x4_t kx[L4], vx[L4];
+#pragma unroll
+            for (int i = 0; i < L4; ++i) {
+                kx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, (i * BMF + lane) * 16, 0, 0));
+                vx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (i * BMF + lane) * 16, 0, 0));
+            }
+#pragma unroll
+            for (int i = 0; i < L4; ++i) {
+                *(f32x4_t*)(&ks[0][0] + (i * BMF + lane) * 4) = kx[i];
+                *(f32x4_t*)(&vs[0][0] + (i * BMF + lane) * 4) = vx[i];
+            }
         }
         __syncthreads();
+        if (t >= n_tiles) continue;
 
+        // S for the tile's 16 keys: 16 independent accumulators, K read as 4-wide broadcasts
         float s[BNF];
+#pragma unroll
+        for (int jj = 0; jj < BNF; ++jj) s[jj] = 0.f;
+#pragma unroll 2
+        for (int d = 0; d < D; d += 4) {
+            // all 16 broadcasts of this 4-column slice are requested before the first FMA, so one
+            // wave per SIMD pays the LDS latency once per slice, not once per key
+            f32x4_t kq[BNF];
+#pragma unroll
+            for (int jj = 0; jj < BNF; ++jj) kq[jj] = *(const f32x4_t*)&ks[jj][d];
+            const float q0v = qs[lane][d], q1v = qs[lane][d + 1], q2v = qs[lane][d + 2], q3v = qs[lane][d + 3];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < BNF; ++jj) {
+                s[jj] = __builtin_fmaf(q0v, kq[jj][0], s[jj]);
+                s[jj] = __builtin_fmaf(q1v, kq[jj][1], s[jj]);
+                s[jj] = __builtin_fmaf(q2v, kq[jj][2], s[jj]);
+                s[jj] = __builtin_fmaf(q3v, kq[jj][3], s[jj]);
+            }
+        }
         float mt = -INFINITY;
 #pragma unroll
         for (int jj = 0; jj < BNF; ++jj) {
-            float acc = 0.f;
-#pragma unroll 16
-            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qs[tid][d], ks[jj][d], acc);
-            const float t = (j0 + jj >= lo && j0 + jj < hi) ? acc * c2 : -INFINITY;
-            s[jj] = t;
-            mt = fmaxf(mt, t);
+            const float tv = (j0 + jj >= lo && j0 + jj < hi) ? s[jj] * c2 : -INFINITY;
+            s[jj] = tv;
+            mt = fmaxf(mt, tv);
         }
         const float m_new = fmaxf(m_run, mt);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -87,24 +152,67 @@ __global__ void __launch_bounds__(BMF) attn_fwd_f32_kernel(attn::Params p) {
         l_run = l_run * alpha + ls;
         m_run = m_new;
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            float acc = o[d] * alpha;
+        for (int d = 0; d < D; d += 4) {
+            float a0 = o[d] * alpha, a1 = o[d + 1] * alpha, a2 = o[d + 2] * alpha, a3 = o[d + 3] * alpha;
+            f32x4_t vv[BNF];  // as for K: the slice's 16 broadcasts first
 #pragma unroll
-            for (int jj = 0; jj < BNF; ++jj) acc = __builtin_fmaf(s[jj], vs[jj][d], acc);
-            o[d] = acc;
+            for (int jj = 0; jj < BNF; ++jj) vv[jj] = *(const f32x4_t*)&vs[jj][d];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 0; jj < BNF; ++jj) {
+                const f32x4_t vq = vv[jj];
+                a0 = __builtin_fmaf(s[jj], vq[0], a0);
+                a1 = __builtin_fmaf(s[jj], vq[1], a1);
+                a2 = __builtin_fmaf(s[jj], vq[2], a2);
+                a3 = __builtin_fmaf(s[jj], vq[3], a3);
+            }
+            o[d] = a0;
+            o[d + 1] = a1;
+            o[d + 2] = a2;
+            o[d + 3] = a3;
         }
     }
 
-    if (qi < p.Nq) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    // Combine the waves' partial states of each row (base 2): M = max_w m_w, l = sum_w 2^(m_w - M) l_w,
+    // O = sum_w 2^(m_w - M) O_w.  A wave that saw no key of the row has m = -inf and weight 0.
+    __syncthreads();
+    part_m[wave][lane] = m_run;
+    part_l[wave][lane] = l_run;
+    __syncthreads();
+    float m_all = part_m[0][lane];
+#pragma unroll
+    for (int w = 1; w < NWF; ++w) m_all = fmaxf(m_all, part_m[w][lane]);
+    const float m_ref = m_all == -INFINITY ? 0.f : m_all;
+    float l_all = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWF; ++w) l_all += part_l[w][lane] * __builtin_amdgcn_exp2f(part_m[w][lane] - m_ref);
+    const float wgt = __builtin_amdgcn_exp2f(m_run - m_ref);
+    float (*const os)[D + 1] = reinterpret_cast<float (*)[D + 1]>(&kv[0][0][0][0]);
+    // waves NWF-1 .. 1 add their weighted outputs into os in turn; wave 0 adds its own and stores
+    for (int w = NWF - 1; w >= 1; --w) {
+        if (wave == w) {
+            if (w == NWF - 1) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) os[lane][d] = o[d] * wgt;
+            } else {
+#pragma unroll
+                for (int d = 0; d < D; ++d) os[lane][d] += o[d] * wgt;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (wave == 0 && qi < p.Nq) {
+        const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
         const size_t row = p.n_splits > 1 ? ((size_t)bw.split * p.B * p.H + bh) * p.Nq + qi
                                           : (size_t)bh * p.Nq + qi;
         float* og = (p.n_splits > 1 ? p.o_part : (float*)p.o) + row * D;
         float* lg = p.n_splits > 1 ? p.lse_part : p.lse;
 #pragma unroll
         for (int d = 0; d < D; d += 4)
-            *(float4*)(og + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-        lg[row] = l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * attn::kLn2 : -INFINITY;
+            *(float4*)(og + d) = make_float4((os[lane][d] + o[d] * wgt) * inv, (os[lane][d + 1] + o[d + 1] * wgt) * inv,
+                                             (os[lane][d + 2] + o[d + 2] * wgt) * inv, (os[lane][d + 3] + o[d + 3] * wgt) * inv);
+        lg[row] = l_all > 0.f ? (m_all + __builtin_amdgcn_logf(l_all)) * attn::kLn2 : -INFINITY;
     }
 }
 
@@ -112,7 +220,7 @@ template <int D>
 hipError_t launch_one(const attn::Params& p, hipStream_t stream) {
     attn::Params pc = p;
     void* args[] = {&pc};
-    return hipLaunchKernel((const void*)attn_fwd_f32_kernel<D>, dim3(p.n_blocks), dim3(BMF), args,
+    return hipLaunchKernel((const void*)attn_fwd_f32_kernel<D>, dim3(p.n_blocks), dim3(BMF * waves_f32<D>()), args,
                            0, stream);
 }
 
