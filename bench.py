@@ -1,6 +1,7 @@
 """Benchmark: fused attention forward on one MI355X, long-context causal workload by default.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--no-cpu-baseline]
+                    [--cold] [--cpu-threads N]
 
 One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
 resident in HBM; attn_decode, key splits and merge, for the KV-cache decode workloads, whose
@@ -9,9 +10,17 @@ attn_bwd, both of its kernels, on the forward's O and LSE and a seeded dO).  W u
 synchronisation, timed with HIP events recorded on the stream the kernel is launched on.
 Prints ONE JSON line on stdout (everything else goes to stderr).
 
+--cold reads a 512 MiB buffer before every step (outside the step's event pair), which evicts
+the L2 caches and the 256 MB MALL and leaves only clean lines in them (a write would leave dirty
+lines whose write-back then competes with the step's reads); the line then reports the median
+per-launch time instead of the region average, since the region holds the flushes.  Every line
+also gives the median and minimum per-launch times and the device memory the steps allocated
+(torch's peak counter and the driver's free-memory count, both expected unchanged: the library
+allocates nothing).
+
 The CPU baseline times the fp64 oracle, untouched, on a bounded random sample of the same
 workload's rows and scales it to the same unit; the same rows are compared with the GPU
-output.  Only this leg loads the oracle.
+output.  Only this leg loads the oracle.  --cpu-threads N limits it to N OpenMP threads.
 """
 from __future__ import annotations
 
@@ -80,14 +89,25 @@ def bwd_algorithmic_bytes(w) -> float:
     return eb * (4 * nq + 4 * nk) + 4 * w.B * w.H * w.Nq
 
 
-def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234, nthreads: int = 0):
     """Time the oracle's backward on whole (b, h) slices (random, growing until ~target_s / 2)."""
     import numpy as np
 
     import oracle
 
     impl = oracle.default()
-    cores = impl.max_threads()
+    cores = nthreads if nthreads > 0 else impl.max_threads()
     rng = np.random.default_rng(seed)
     order = rng.permutation(w.B * w.H)
     args = (x["q"], x["k"], x["v"], do, w.dtype, float(x["scale"]), w.causal, x["key_lens"])
@@ -98,7 +118,7 @@ def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
         if sel.size == 0:
             break
         t0 = time.perf_counter()
-        want = impl.attn_bwd(*args, None, sel, **wkw)
+        want = impl.attn_bwd(*args, None, sel, nthreads=nthreads, **wkw)
         spent += time.perf_counter() - t0
         done.append((sel, want))
         if spent >= 0.5 * target_s:
@@ -121,6 +141,7 @@ def cpu_baseline_bwd(w, x, do, grads, target_s: float, seed: int = 1234):
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{slices.size} random (b, h) slices of the same workload (seed {seed}), fp64 oracle "
                   f"backward with {cores} OpenMP threads, {spent:.2f} s; flops counted as 2.5 x 4*D per "
@@ -152,7 +173,7 @@ def row_pairs(w, rows, key_lens):
     return np.maximum(hi - np.maximum(i - w.window, 0), 0)
 
 
-def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
+def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234, nthreads: int = 0):
     """Time the oracle on a random sample of rows (pilot run, then ~target_s of work)."""
     import numpy as np
     import torch
@@ -160,7 +181,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
     import oracle
 
     impl = oracle.default()
-    cores = impl.max_threads()
+    cores = nthreads if nthreads > 0 else impl.max_threads()
     rng = np.random.default_rng(seed)
     total = w.B * w.H * w.Nq
     args = (x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), oracle_causal(w), x["key_lens"])
@@ -171,7 +192,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
         n = min(n, total)
         rows = np.sort(rng.choice(total, size=n, replace=False)) if n < total else np.arange(total)
         t0 = time.perf_counter()
-        ro, rl = impl.attn_rows(*args, rows=rows, window=w.window)
+        ro, rl = impl.attn_rows(*args, rows=rows, nthreads=nthreads, window=w.window)
         dt = time.perf_counter() - t0
         if dt >= 0.5 * target_s or n >= total:
             break
@@ -181,7 +202,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
         reps = max(1, int(0.5 * target_s / max(dt, 1e-3)))
         t0 = time.perf_counter()
         for _ in range(reps):
-            ro, rl = impl.attn_rows(*args, rows=rows, window=w.window)
+            ro, rl = impl.attn_rows(*args, rows=rows, nthreads=nthreads, window=w.window)
         dt = (time.perf_counter() - t0) / reps
     pairs = float(row_pairs(w, rows, x["key_lens"]).sum())
     flops = 4.0 * w.D * pairs
@@ -205,6 +226,7 @@ def cpu_baseline(w, x, o_dev, lse_dev, target_s: float, seed: int = 1234):
         "value": value,
         "unit": unit,
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{rows.size} random query rows of the same workload (seed {seed}), fp64 oracle "
                   f"with {cores} OpenMP threads, {dt:.3f} s per pass ({reps} passes); {counted}",
@@ -224,6 +246,9 @@ def main():
                     help="time the forward (default) or the backward (attn_bwd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-threads", type=int, default=0, help="OpenMP threads of the CPU baseline (0: all)")
+    ap.add_argument("--cold", action="store_true",
+                    help="evict L2 and MALL (512 MiB read) before every step; report the median launch time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference dispatch for HBM byte counters)")
@@ -317,10 +342,16 @@ def main():
             if rc != binding.ATTN_OK:
                 raise binding.AttnError(rc)
 
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev) if a.cold else None  # 512 MiB
     for _ in range(a.warmup):
+        if flush is not None:
+            flush.sum()
         step()
     torch.cuda.synchronize(dev)
     log(f"[bench] warm-up done ({a.warmup} steps)")
+    alloc0 = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    free0 = torch.cuda.mem_get_info(dev)[0]
 
     # Timed region: K steps; an event pair around every launch on the launch stream.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
@@ -331,16 +362,22 @@ def main():
     wall0 = time.perf_counter()
     region0.record(stream)
     for i in range(a.steps):
+        if flush is not None:
+            flush.sum()
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     region1.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
+    free1 = torch.cuda.mem_get_info(dev)[0]
+    peak_alloc = torch.cuda.max_memory_allocated(dev) - alloc0
     region_ms = region0.elapsed_time(region1)
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    ms_per_step = region_ms / a.steps
+    med_launch_ms = sorted(launch_ms)[len(launch_ms) // 2]
+    # with --cold the region holds the flushes: the step time is the median launch
+    ms_per_step = med_launch_ms if a.cold else region_ms / a.steps
     log(f"[bench] {a.steps} steps: region {region_ms:.3f} ms, {ms_per_step:.4f} ms/step, "
         f"avg launch {avg_launch_ms:.4f} ms (min {min(launch_ms):.4f}), wall {wall:.3f} s")
 
@@ -401,11 +438,14 @@ def main():
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
                    "causal": w.causal, "key_padding": w.padded, "window": w.window,
                    "kv_cache": w.kv_cache, "pass": a.which, "seed": x["seed"],
-                   "parallelism": "none (1 GPU)"},
+                   "cache": "cold" if a.cold else "warm", "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "roofline": roofline,
         "tflops": tflops,
         "avg_launch_ms": avg_launch_ms,
+        "median_launch_ms": med_launch_ms,
+        "min_launch_ms": min(launch_ms),
+        "step_alloc_bytes": {"torch_peak": int(peak_alloc), "device_free_delta": int(free0 - free1)},
         "algorithmic_bytes": abytes,
         "algorithmic_gbs": abytes / (avg_launch_ms * 1e-3) / 1e9,
         "kernel_source_sha256": src_hash,
@@ -413,13 +453,13 @@ def main():
     }
     if not a.no_cpu_baseline and bwd:
         log(f"[bench] cpu baseline: oracle backward on sampled slices (~{a.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline_bwd(w, x, do_np, grads, a.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_bwd(w, x, do_np, grads, a.cpu_seconds, nthreads=a.cpu_threads)
         cb = result["cpu_baseline"]
         log(f"[bench] cpu baseline {cb['value']:.4g} {cb['unit']} on {cb['cores']} threads; "
             f"sample max relative gradient error {cb['sample_max_rel_err_grads']:.3e}")
     elif not a.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on a sample (~{a.cpu_seconds:.0f} s)")
-        result["cpu_baseline"] = cpu_baseline(w, x, o, lse, a.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, x, o, lse, a.cpu_seconds, nthreads=a.cpu_threads)
         cb = result["cpu_baseline"]
         log(f"[bench] cpu baseline {cb['value']:.4g} {cb['unit']} on {cb['cores']} threads; "
             f"sample max|dO|={cb['sample_max_abs_err_o']:.3e} max|dLSE|={cb['sample_max_abs_err_lse']:.3e}")

@@ -122,6 +122,23 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int qw0 = q0 + wave * 32;
     const int qi = qw0 + r;
 
+    const T* qg = (const T*)p.q + (size_t)bh * p.Nq * D;
+    const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
+    const T* vg = (const T*)p.v + (size_t)bh * p.Nk * D;
+
+    // Q^T operand: lane (r, g) holds Q[qi][16 ks + 8 g .. +7]; rows past Nq read as 0.  Requested
+    // first, so that the key-length load and the first K/V tile overlap it (its sign flip, when
+    // asked for, waits until both are issued).
+    u32x4_t qraw[KSTEPS];
+    {
+        const __amdgpu_buffer_rsrc_t qrs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, p.Nq * D * 2, kBufferWord3);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            qraw[ks] = __builtin_amdgcn_raw_buffer_load_b128(qrs, (qi * D + 16 * ks + 8 * g) * 2, 0, 0);
+    }
+    vec8 qf[KSTEPS];  // qraw with the sign flip applied, set once the first tile is requested
+
     // Key tiles [t_begin, n_tiles) hold every key some row of this workgroup may see.
     const int kv_valid = attn::clamp_len(p.key_lens, b, p.Nk);
     const int q_last = min(p.Nq, q0 + BM) - 1;
@@ -133,23 +150,6 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     }
     const int n_tiles = (kv_end + BN - 1) / BN;
     const int t_begin = k_begin / BN;
-
-    const T* qg = (const T*)p.q + (size_t)bh * p.Nq * D;
-    const T* kg = (const T*)p.k + (size_t)bh * p.Nk * D;
-    const T* vg = (const T*)p.v + (size_t)bh * p.Nk * D;
-
-    // Q^T operand: lane (r, g) holds Q[qi][16 ks + 8 g .. +7]; rows past Nq read as 0.
-    vec8 qf[KSTEPS];
-    {
-        const __amdgpu_buffer_rsrc_t qrs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)qg, 0, p.Nq * D * 2, kBufferWord3);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(qrs, (qi * D + 16 * ks + 8 * g) * 2, 0, 0);
-            if (p.negate_q) x ^= 0x80008000u;
-            qf[ks] = __builtin_bit_cast(vec8, x);
-        }
-    }
 
     // Per-lane byte offsets of this thread's tile loads: slot (i*NT + tid) of a tile holds the
     // global 16-byte chunk (row, chunk ^ swizzle(row)).
@@ -319,6 +319,9 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     };
 
     if (t_begin < n_tiles) issue_tile(t_begin, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+        qf[ks] = __builtin_bit_cast(vec8, p.negate_q ? qraw[ks] ^ 0x80008000u : qraw[ks]);
     for (int it = t_begin; it < n_tiles; it += 2) {
         do_tile(it, 0);
         if (it + 1 < n_tiles) do_tile(it + 1, 1);
