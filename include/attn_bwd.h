@@ -17,6 +17,16 @@
 
 #include "attn_fwd.h"
 
+/* The entry points are the only symbols the library exports (it is built with hidden
+ * visibility); ATTN_API marks them. */
+#ifndef ATTN_API
+#if defined(__GNUC__) || defined(__clang__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -44,10 +54,10 @@ extern "C" {
  * ATTN_ERR_NULL / ATTN_ERR_ALIGN / ATTN_ERR_WORKSPACE for a missing, misaligned or short
  * workspace and ATTN_ERR_DTYPE for ATTN_F32.  Outputs must not alias inputs.
  */
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
-             int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
-             void* workspace, size_t workspace_bytes, void* stream);
+ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
+                      int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_bwd_window -- attn_bwd for the forward of attn_fwd_window: the gradients of attention
@@ -57,15 +67,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
  * attn_fwd_window with the same window.  Key and query tiles outside every band are skipped.
  * Other arguments, layout, workspace, ownership and errors as attn_bwd.
  */
-int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
-                    int Nq, int Nk, int D, float scale, int causal, int window,
-                    const int32_t* key_lens, int dtype, void* workspace, size_t workspace_bytes,
-                    void* stream);
+ATTN_API int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,
+                             int Nq, int Nk, int D, float scale, int causal, int window,
+                             const int32_t* key_lens, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Workspace bytes attn_bwd needs: 2 * B * H * round_up(Nq, 64) * 4; 0 for B, H or Nq < 1.
  * attn_bwd returns ATTN_ERR_SHAPE when this exceeds 2^31 - 1 bytes. */
-size_t attn_bwd_workspace_size(int B, int H, int Nq);
+ATTN_API size_t attn_bwd_workspace_size(int B, int H, int Nq);
 
 #ifdef __cplusplus
 }

@@ -29,6 +29,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* The entry points are the only symbols the library exports (it is built with hidden
+ * visibility); ATTN_API marks them. */
+#ifndef ATTN_API
+#if defined(__GNUC__) || defined(__clang__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -82,9 +92,9 @@ typedef enum {
  * the runtime returns ATTN_ERR_LAUNCH.  Faults inside the kernel (e.g. a pointer that is not
  * device memory of the stated size) surface on the stream, not here.
  */
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
-             void* stream);
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                      int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+                      void* stream);
 
 /*
  * attn_fwd_window -- attn_fwd restricted to a local band (sliding-window attention): row i
@@ -101,9 +111,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
  *   ATTN_ERR_WINDOW and writes nothing.  A row whose band holds no valid key gets O = 0 and
  *   LSE = -inf.
  */
-int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                    int H, int Nq, int Nk, int D, float scale, int causal, int window,
-                    const int32_t* key_lens, int dtype, void* stream);
+ATTN_API int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                             int H, int Nq, int Nk, int D, float scale, int causal, int window,
+                             const int32_t* key_lens, int dtype, void* stream);
 
 /*
  * attn_decode -- attention of Nq new queries against a KV cache: the queries are the last Nq
@@ -128,18 +138,18 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  * workspace and ATTN_ERR_WORKSPACE when it is too small; nothing is enqueued on any error.
  * Calls that share a workspace must not overlap in time.
  */
-int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
-                void* workspace, size_t workspace_bytes, void* stream);
+ATTN_API int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                         int Nq, int Nk, int D, float scale, int causal, const int32_t* key_lens, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_workspace_size -- bytes of workspace attn_decode needs for these sizes (0 when it
  * needs none, or when the sizes are invalid).  A pure function of its arguments.
  */
-size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D, int dtype);
+ATTN_API size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D, int dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
-const char* attn_status_str(int status);
+ATTN_API const char* attn_status_str(int status);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,9 @@ def test_library_exports_every_declared_symbol():
                          text=True, check=True).stdout
     for name in declared_functions():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} is not a defined text symbol"
+    # and nothing else: launchers and kernels stay internal (hidden visibility)
+    exported = set(re.findall(r"\bT (\S+)$", out, flags=re.M))
+    assert exported == set(declared_functions()), f"unexpected exports: {sorted(exported - set(declared_functions()))}"
 
 
 def test_status_strings():

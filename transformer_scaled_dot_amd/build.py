@@ -19,7 +19,7 @@ HEADERS = ["attn_common.h", "attn_bwd.h", os.path.join(ROOT, "include", "attn_fw
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     # packed fp32 arithmetic stays off: the compiler would otherwise form v_pk_* fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
