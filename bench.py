@@ -2,6 +2,7 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--no-cpu-baseline]
                     [--cold] [--cpu-threads N]
+    python bench.py --gemm-reference N   (vendor bf16 GEMM rate, for scale)
 
 One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
 resident in HBM; attn_decode, key splits and merge, for the KV-cache decode workloads, whose
@@ -247,6 +248,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-threads", type=int, default=0, help="OpenMP threads of the CPU baseline (0: all)")
+    ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
+                    help="instead of attention, time torch's bf16 N x N x N matmul (the vendor GEMM) "
+                         "as a reference for what dense MFMA work sustains on this GPU")
     ap.add_argument("--cold", action="store_true",
                     help="evict L2 and MALL (512 MiB read) before every step; report the median launch time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -265,6 +269,27 @@ def main():
     import torch
 
     from transformer_scaled_dot_amd import binding, inputs
+
+    if a.gemm_reference > 0:
+        n = a.gemm_reference
+        x0 = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        x1 = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(a.warmup):
+            torch.matmul(x0, x1)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            torch.matmul(x0, x1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"metric": "reference: vendor bf16 GEMM TFLOP/s (torch.matmul)", "value": tf,
+                          "unit": "TFLOP/s", "ms_per_step": ms, "steps": a.steps, "warmup": a.warmup,
+                          "config": {"workload": f"gemm_bf16_{n}x{n}x{n}"},
+                          "frac_of_peak": tf / PEAK_TFLOPS["bf16"]}), flush=True)
+        return
 
     name = a.workload or inputs.BENCH_WORKLOAD
     w = inputs.WORKLOADS[name]
