@@ -14,10 +14,10 @@ namespace {
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr int NT = 256;  // threads per row
 
-// One workgroup per query row.  Wave 0 turns the splits' LSEs (one per lane, S <= 64) into
-// normalised weights w_s = e^{LSE_s - LSE}; then every thread owns one float4 column of O and
-// every (NT / (D/4))-th split, so all of a row's partial-O loads are in flight at once, and
-// the per-group sums meet in LDS.
+// One workgroup per query row.  Every thread owns one float4 column of O and every
+// (NT / (D/4))-th split, and requests its partial-O values first, so that all of a row's loads
+// are in flight while wave 0 turns the splits' LSEs (one per lane, S <= 64) into normalised
+// weights w_s = e^{LSE_s - LSE}; the per-group weighted sums then meet in LDS.
 template <typename T, int D>
 __global__ void __launch_bounds__(NT) attn_merge_kernel(attn::Params p) {
     constexpr int C4 = D / 4;     // float4 columns per row
@@ -29,6 +29,15 @@ __global__ void __launch_bounds__(NT) attn_merge_kernel(attn::Params p) {
     const size_t row = blockIdx.x;  // (b * H + h) * Nq + i
     const size_t plane = (size_t)p.B * p.H * p.Nq;
     const int S = p.n_splits;
+
+    constexpr int KS = 64 / NG;  // splits per thread
+    const int g = tid / C4, c = tid - g * C4;
+    float4 v[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int sp = g + k * NG;
+        v[k] = sp < S ? *((const float4*)(p.o_part + (sp * plane + row) * D) + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 
     if (tid < 64) {
         const float ls = tid < S ? p.lse_part[tid * plane + row] : -INFINITY;
@@ -44,18 +53,16 @@ __global__ void __launch_bounds__(NT) attn_merge_kernel(attn::Params p) {
     }
     __syncthreads();
 
-    const int g = tid / C4, c = tid - g * C4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < 64 / NG; ++k) {
+    for (int k = 0; k < KS; ++k) {
         const int sp = g + k * NG;
         if (sp < S) {
             const float w = wsh[sp];
-            const float4 v = *((const float4*)(p.o_part + (sp * plane + row) * D) + c);
-            acc.x = __builtin_fmaf(w, v.x, acc.x);
-            acc.y = __builtin_fmaf(w, v.y, acc.y);
-            acc.z = __builtin_fmaf(w, v.z, acc.z);
-            acc.w = __builtin_fmaf(w, v.w, acc.w);
+            acc.x = __builtin_fmaf(w, v[k].x, acc.x);
+            acc.y = __builtin_fmaf(w, v[k].y, acc.y);
+            acc.z = __builtin_fmaf(w, v[k].z, acc.z);
+            acc.w = __builtin_fmaf(w, v[k].w, acc.w);
         }
     }
     red[g][c] = acc;
