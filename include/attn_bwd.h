@@ -42,7 +42,8 @@ extern "C" {
  *   dq          device, [B, H, Nq, D], `dtype` (written).
  *   dk, dv      device, [B, H, Nk, D], `dtype` (written; keys no row sees get 0).
  *   B, H, Nq, Nk, D, scale, key_lens  as attn_fwd; causal 0 or 1 (top-left).
- *   dtype       ATTN_BF16 or ATTN_F16 (fp32 accumulation; outputs rounded to nearest even).
+ *   dtype       ATTN_BF16 or ATTN_F16 (fp32 accumulation; outputs rounded to nearest even), or
+ *               ATTN_F32 (fp32 throughout, on the vector ALUs: meant for small problems).
  *   workspace   device memory of at least attn_bwd_workspace_size(B, H, Nq) bytes, 16-byte
  *               aligned, owned by the caller; contents on entry do not matter (overwritten).
  *   stream      hipStream_t as void*, NULL for the default stream.
@@ -52,7 +53,7 @@ extern "C" {
  * workspace must not overlap in time.  Alignment: every tensor pointer 16-byte aligned,
  * key_lens 4-byte.  Errors as attn_fwd (checked on the host, nothing enqueued on error), plus
  * ATTN_ERR_NULL / ATTN_ERR_ALIGN / ATTN_ERR_WORKSPACE for a missing, misaligned or short
- * workspace and ATTN_ERR_DTYPE for ATTN_F32.  Outputs must not alias inputs.
+ * workspace.  Outputs must not alias inputs.
  */
 ATTN_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, const float* dlse, void* dq, void* dk, void* dv, int B, int H,

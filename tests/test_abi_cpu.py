@@ -148,7 +148,7 @@ BWD_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dlse=None, dq=F
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), -1), (dict(do=None), -1), (dict(dv=None), -1), (dict(lse=None), -1),
-    (dict(B=0), -2), (dict(Nk=0), -2), (dict(D=96), -3), (dict(dtype=0), -4), (dict(dtype=3), -4),
+    (dict(B=0), -2), (dict(Nk=0), -2), (dict(D=96), -3), (dict(dtype=-1), -4), (dict(dtype=3), -4),
     (dict(scale=float("nan")), -5), (dict(causal=2), -6), (dict(dq=FAKE + 4), -8),
     (dict(dlse=FAKE + 4), -8), (dict(key_lens=FAKE + 1), -8), (dict(ws=None), -1),
     (dict(ws=FAKE + 8), -8), (dict(ws_bytes=2 * 2 * 3 * 64 * 4 - 1), -10), (dict(Nq=1 << 22, D=128), -2),
@@ -175,7 +175,7 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(window=-2), -9), (dict(window=-1000), -9), (dict(q=None), -1), (dict(dtype=0), -4),
+    (dict(window=-2), -9), (dict(window=-1000), -9), (dict(q=None), -1), (dict(dtype=3), -4),
     (dict(causal=2), -6), (dict(ws=None), -1),
 ])
 def test_host_validation_bwd_window(over, code):

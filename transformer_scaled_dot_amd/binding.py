@@ -254,7 +254,7 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: fl
         dlse=None, dq=None, dk=None, dv=None, workspace=None, stream=None, window: int | None = None):
     """dQ, dK, dV of attention(q, k, v) for the gradient `dout` of O (and `dlse` of LSE, or None).
     o and lse are the forward's outputs for the same q, k, v, causal, key_lens, scale and window.
-    Tensors as for fwd (bf16 or fp16); returns (dq, dk, dv) in q's dtype."""
+    Tensors as for fwd (fp32, bf16 or fp16); returns (dq, dk, dv) in q's dtype."""
     if window is not None and (int(window) != window or window < 0):
         raise ValueError("window must be None or an integer >= 0")
     torch = _torch()
@@ -262,8 +262,6 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: fl
                                                                        stream)
     if out is not o or lse_t is not lse:
         raise ValueError("o and lse must be the forward's outputs")
-    if code == ATTN_F32:
-        raise ValueError("the backward takes bfloat16 or float16 tensors")
     if not isinstance(dout, torch.Tensor) or dout.shape != q.shape or dout.dtype != q.dtype \
             or dout.device != q.device or not dout.is_contiguous():
         raise ValueError("dout must be a contiguous tensor like q")

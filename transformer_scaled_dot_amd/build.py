@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn_fwd.so")
 SOURCES = ["attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip",
-           "attn_bwd_api.hip", "attn_bwd_mfma.hip"]
+           "attn_bwd_api.hip", "attn_bwd_mfma.hip", "attn_bwd_f32.hip"]
 HEADERS = ["attn_common.h", "attn_bwd.h", os.path.join(ROOT, "include", "attn_fwd.h"),
            os.path.join(ROOT, "include", "attn_bwd.h")]
 

@@ -61,3 +61,7 @@ __device__ __forceinline__ int bwd_row_hi(const BwdParams& p, int j) {
 hipError_t attn_launch_bwd_mfma(const attn::BwdParams& p, int dtype, int D, hipStream_t stream);
 int attn_bwd_q_block();   // query rows per dQ workgroup
 int attn_bwd_k_block();   // keys per dK/dV workgroup
+// fp32 storage: the vector-ALU kernels of attn_bwd_f32.hip
+hipError_t attn_launch_bwd_f32(const attn::BwdParams& p, int D, hipStream_t stream);
+int attn_bwd_f32_q_block();
+int attn_bwd_f32_k_block();

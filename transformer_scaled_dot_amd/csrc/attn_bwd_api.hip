@@ -26,7 +26,7 @@ extern "C" int attn_bwd_window(const void* q, const void* k, const void* v, cons
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
     if (D != 64 && D != 128) return ATTN_ERR_HEAD_DIM;
-    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (dtype != ATTN_F32 && dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (!isfinite(scale)) return ATTN_ERR_SCALE;
     if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
     if (window < -1) return ATTN_ERR_WINDOW;
@@ -35,7 +35,9 @@ extern "C" int attn_bwd_window(const void* q, const void* k, const void* v, cons
     if ((ptrs & 15) != 0 || ((uintptr_t)key_lens & 3) != 0) return ATTN_ERR_ALIGN;
     if ((int64_t)Nq * D >= ((int64_t)1 << 29) || (int64_t)Nk * D >= ((int64_t)1 << 29)) return ATTN_ERR_SHAPE;
 
-    const int64_t bm = attn_bwd_q_block(), bn = attn_bwd_k_block();
+    const bool f32 = dtype == ATTN_F32;
+    const int64_t bm = f32 ? attn_bwd_f32_q_block() : attn_bwd_q_block();
+    const int64_t bn = f32 ? attn_bwd_f32_k_block() : attn_bwd_k_block();
     const int64_t n_qtiles = ((int64_t)Nq + bm - 1) / bm, n_ktiles = ((int64_t)Nk + bn - 1) / bn;
     const int64_t nbq = n_qtiles * H * B, nbk = n_ktiles * H * B;
     const int64_t pad = nq_padded(Nq);
@@ -77,7 +79,9 @@ extern "C" int attn_bwd_window(const void* q, const void* k, const void* v, cons
     p.causal = causal;
     // |i - j| < max(Nq, Nk) always holds: a band at least that wide is no band
     p.window = window >= (Nq > Nk ? Nq : Nk) ? -1 : window;
-    return attn_launch_bwd_mfma(p, dtype, D, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    const hipError_t e = f32 ? attn_launch_bwd_f32(p, D, (hipStream_t)stream)
+                             : attn_launch_bwd_mfma(p, dtype, D, (hipStream_t)stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
