@@ -45,7 +45,7 @@ METRIC_BWD = "attention bwd TFLOP/s (2.5 x the forward's 4·B·H·N²·D, causal
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["attn_common.h", "attn_fwd_api.hip", "attn_fwd_mfma.hip", "attn_fwd_f32.hip", "attn_merge.hip"]
-BWD_KERNEL_SOURCES = ["attn_common.h", "attn_bwd.h", "attn_bwd_api.hip", "attn_bwd_mfma.hip"]
+BWD_KERNEL_SOURCES = ["attn_common.h", "attn_bwd.h", "attn_bwd_api.hip", "attn_bwd_mfma.hip", "attn_bwd_f32.hip"]
 
 
 def log(*a):
