@@ -2,8 +2,8 @@
 marshalling only).
 
 `attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size`, `attn_bwd`,
-`attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one to one (raw
-device pointers, sizes, a stream handle).  `fwd`, `decode` and `bwd` are the tensor-level
+`attn_bwd_window`, `attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one
+to one (raw device pointers, sizes, a stream handle).  `fwd`, `decode` and `bwd` are the tensor-level
 conveniences: they check the tensors on the host, allocate the outputs (and workspaces) with
 torch on the current stream and call the matching entry point.  Every step of
 the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
@@ -34,7 +34,7 @@ _lib = None
 class AttnError(RuntimeError):
     def __init__(self, status: int):
         self.status = status
-        super().__init__(f"attn_fwd failed: {STATUS.get(status, status)} ({attn_status_str(status)})")
+        super().__init__(f"attention call failed: {STATUS.get(status, status)} ({attn_status_str(status)})")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -153,7 +153,7 @@ def dtype_code(t) -> int:
 
 
 def _check(q, k, v, key_lens, scale, out, lse, stream):
-    """Host checks shared by fwd and decode; returns the marshalled arguments."""
+    """Host checks shared by fwd, decode and bwd; returns the marshalled arguments."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
