@@ -1,7 +1,7 @@
 """Benchmark: fused attention forward on one MI355X, long-context causal workload by default.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--pass fwd|bwd] [--no-cpu-baseline]
-                    [--cold] [--cpu-threads N]
+                    [--cold] [--graph] [--cpu-threads N]
     python bench.py --gemm-reference N   (vendor bf16 GEMM rate, for scale)
 
 One step = one call of the whole hot path (attn_fwd over one batch of synthetic input already
@@ -11,6 +11,8 @@ attn_bwd, both of its kernels, on the forward's O and LSE and a seeded dO).  W u
 synchronisation, timed with HIP events recorded on the stream the kernel is launched on.
 Prints ONE JSON line on stdout (everything else goes to stderr).
 
+--graph captures one step in a HIP graph and times replays of it: the per-step time then holds
+no host launch cost (what a serving loop that replays graphs pays for the tiny cases).
 --cold reads a 512 MiB buffer before every step (outside the step's event pair), which evicts
 the L2 caches and the 256 MB MALL and leaves only clean lines in them (a write would leave dirty
 lines whose write-back then competes with the step's reads); the line then reports the median
@@ -251,6 +253,8 @@ def main():
     ap.add_argument("--gemm-reference", type=int, default=0, metavar="N",
                     help="instead of attention, time torch's bf16 N x N x N matmul (the vendor GEMM) "
                          "as a reference for what dense MFMA work sustains on this GPU")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time replays of it (no host launch cost)")
     ap.add_argument("--cold", action="store_true",
                     help="evict L2 and MALL (512 MiB read) before every step; report the median launch time")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -340,8 +344,8 @@ def main():
         args = (*ptrs[:4], do.data_ptr(), lse.data_ptr(), None, *(t.data_ptr() for t in grads), *dims,
                 win, kl_ptr, code, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
 
-        def step():
-            rc = lib.attn_bwd_window(*args)
+        def step(handle=None):  # handle: the stream to enqueue on (default: the bench's stream)
+            rc = lib.attn_bwd_window(*args[:-1], args[-1] if handle is None else handle)
             if rc != binding.ATTN_OK:
                 raise binding.AttnError(rc)
     elif w.kv_cache:
@@ -352,8 +356,8 @@ def main():
                        workspace=workspace, stream=stream)
         args = (*ptrs, *dims, kl_ptr, code, workspace.data_ptr(), ws_bytes, stream.cuda_stream)
 
-        def step():
-            rc = lib.attn_decode(*args)
+        def step(handle=None):  # handle: the stream to enqueue on (default: the bench's stream)
+            rc = lib.attn_decode(*args[:-1], args[-1] if handle is None else handle)
             if rc != binding.ATTN_OK:
                 raise binding.AttnError(rc)
     else:
@@ -362,11 +366,30 @@ def main():
         win = -1 if w.window is None else min(int(w.window), 2**31 - 1)
         args = (*ptrs, *dims, win, kl_ptr, code, stream.cuda_stream)
 
-        def step():
-            rc = lib.attn_fwd_window(*args)
+        def step(handle=None):  # handle: the stream to enqueue on (default: the bench's stream)
+            rc = lib.attn_fwd_window(*args[:-1], args[-1] if handle is None else handle)
             if rc != binding.ATTN_OK:
                 raise binding.AttnError(rc)
 
+    if a.graph:
+        # One step captured on a side stream; replays then run on the bench's stream.  The entry
+        # points enqueue only kernels (no allocation, memset or host synchronisation), so a
+        # captured call replays exactly.
+        eager_step = step
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            eager_step(side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step(torch.cuda.current_stream(dev).cuda_stream)
+        torch.cuda.synchronize(dev)
+
+        def step(handle=None):
+            graph.replay()
+        log("[bench] timing replays of a captured HIP graph of one step")
     flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev) if a.cold else None  # 512 MiB
     for _ in range(a.warmup):
         if flush is not None:
@@ -463,7 +486,8 @@ def main():
         "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
                    "causal": w.causal, "key_padding": w.padded, "window": w.window,
                    "kv_cache": w.kv_cache, "pass": a.which, "seed": x["seed"],
-                   "cache": "cold" if a.cold else "warm", "parallelism": "none (1 GPU)"},
+                   "cache": "cold" if a.cold else "warm", "launch": "hip graph replay" if a.graph else "eager",
+                   "parallelism": "none (1 GPU)"},
         "pct_of_peak": 100.0 * value / peak,
         "roofline": roofline,
         "tflops": tflops,
