@@ -187,3 +187,13 @@ def test_host_validation_bwd_window(over, code):
                                  a["causal"], a["window"], a["key_lens"], a["dtype"], a["ws"], a["ws_bytes"],
                                  a["stream"])
     assert rc == code
+
+
+def test_c_caller_is_built_and_checks_its_arguments():
+    """The plain C caller (gcc, public header only) is built with the library; given no arguments
+    it prints its usage and exits 1 before any GPU call."""
+    caller = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "c_abi",
+                          "attn_fwd_c_caller")
+    assert os.access(caller, os.X_OK)
+    r = subprocess.run([caller], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
