@@ -1,7 +1,9 @@
-"""MI355X (gfx950) fused multi-head scaled-dot-product attention forward.
+"""MI355X (gfx950) fused multi-head scaled-dot-product attention: forward, KV-cache decode and
+backward.
 
-    from transformer_scaled_dot_amd import fwd
+    from transformer_scaled_dot_amd import fwd, attention
     o, lse = fwd(q, k, v, causal=True)
+    o = attention(q, k, v, causal=True)   # differentiable: o.backward(...) runs the HIP backward
 
 The computation lives in libattn_fwd.so (hand-written HIP kernels behind the C ABI declared in
 include/attn_fwd.h); `binding` marshals arguments to it.  `inputs` is the seeded generator of
@@ -10,7 +12,7 @@ synthetic workloads.  Importing the package loads nothing; the library is loaded
 
 
 def __getattr__(name):
-    if name in ("fwd", "attn_fwd", "attn_status_str", "AttnError", "load_library"):
+    if name in ("fwd", "bwd", "decode", "attention", "attn_fwd", "attn_status_str", "AttnError", "load_library"):
         from . import binding
 
         return getattr(binding, name)

@@ -5,7 +5,8 @@ marshalling only).
 `attn_bwd_window`, `attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one
 to one (raw device pointers, sizes, a stream handle).  `fwd`, `decode` and `bwd` are the tensor-level
 conveniences: they check the tensors on the host, allocate the outputs (and workspaces) with
-torch on the current stream and call the matching entry point.  Every step of
+torch on the current stream and call the matching entry point; `attention` joins the forward
+and the backward into one differentiable op for PyTorch code.  Every step of
 the computation runs in the HIP kernels of libattn_fwd.so; if that library is missing this
 module raises instead of computing anything itself.
 """
@@ -289,3 +290,48 @@ def bwd(q, k, v, o, lse, dout, *, causal: bool = False, key_lens=None, scale: fl
     if rc != ATTN_OK:
         raise AttnError(rc)
     return tuple(outs)
+
+
+def _attention_function():
+    """The torch.autograd.Function behind `attention` (built on first use: importing this module
+    does not import torch)."""
+    global _AttentionFn
+    if _AttentionFn is not None:
+        return _AttentionFn
+    torch = _torch()
+
+    class AttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale, key_lens, window):
+            o, lse = fwd(q, k, v, causal=causal, key_lens=key_lens, scale=scale, window=window)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.key_lens, ctx.causal, ctx.scale, ctx.window = key_lens, causal, scale, window
+            ctx.set_materialize_grads(False)  # an unused output's gradient arrives as None
+            return o, lse
+
+        @staticmethod
+        def backward(ctx, do, dlse):
+            q, k, v, o, lse = ctx.saved_tensors
+            if do is None:  # only the LSE reaches the loss
+                do = torch.zeros_like(o)
+            dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, key_lens=ctx.key_lens,
+                             scale=ctx.scale, dlse=None if dlse is None else dlse.contiguous(),
+                             window=ctx.window)
+            return dq, dk, dv, None, None, None, None
+
+    _AttentionFn = AttentionFn
+    return AttentionFn
+
+
+_AttentionFn = None
+
+
+def attention(q, k, v, *, causal: bool = False, scale: float | None = None, key_lens=None,
+              window: int | None = None, return_lse: bool = False):
+    """Differentiable attention for PyTorch code: O = softmax(scale q k^T + mask) v per (b, h),
+    with the forward and backward of this library (attn_fwd_window / attn_bwd_window) as the
+    two passes.  Tensors as for `fwd` ([B, H, N, D], contiguous, CUDA, fp32 / fp16 / bf16);
+    key_lens (int32 [B]) and window as for `fwd`.  Returns O, or (O, LSE) with return_lse=True,
+    in which case a loss may also depend on LSE (its gradient enters the backward as dLSE)."""
+    o, lse = _attention_function().apply(q, k, v, bool(causal), scale, key_lens, window)
+    return (o, lse) if return_lse else o
