@@ -264,7 +264,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {a.gpus}, "
+        print(f"bench.py: the library runs on exactly one GPU (asked for --gpus {a.gpus}, "
               f"WORLD_SIZE={world}); heads shard across GPUs with no communication, but no "
               f"multi-GPU path is built", file=sys.stderr)
         sys.exit(2)
