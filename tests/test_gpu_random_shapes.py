@@ -1,6 +1,7 @@
 """Seeded random shapes through every entry point, against the oracle (needs an MI355X).
 
-Each case draws B, H, Nq, Nk in [1, 300], D in {64, 128}, a storage type, the causal flag, an
+Each case draws B, H, Nq, Nk in [1, 300] (and 24 larger cases: one or two slices, Nq, Nk in
+[300, 3000], so the decode keys are split over workgroups), D in {64, 128}, a storage type, the causal flag, an
 optional band, key lengths (some zero, some past Nk) and a scale (negative and zero included),
 and checks the forward, the KV-cache decode entry point and (every other case) the backward
 against the oracle at the usual tolerances.  The cases are fixed by the seed, so a failure names
@@ -16,26 +17,41 @@ from transformer_scaled_dot_amd import binding, inputs
 pytestmark = pytest.mark.gpu
 
 N_CASES = 200
+N_LARGE = 24
 TOL_G = {"bf16": (2e-2, 1e-3), "f16": (2e-2, 1e-3), "f32": (1e-4, 1e-1)}
 
 
-def draw(i):
-    r = np.random.default_rng(9000 + i)
-    B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
-    Nq, Nk = int(r.integers(1, 301)), int(r.integers(1, 301))
+def draw(i, large=False):
+    r = np.random.default_rng((19000 if large else 9000) + i)
+    if large:  # longer key loops and split decodes; few slices so the oracle stays quick
+        B, H = 1, int(r.integers(1, 3))
+        Nq, Nk = int(r.integers(300, 3001)), int(r.integers(300, 3001))
+    else:
+        B, H = int(r.integers(1, 4)), int(r.integers(1, 4))
+        Nq, Nk = int(r.integers(1, 301)), int(r.integers(1, 301))
     D = int(r.choice([64, 128]))
     dtype = str(r.choice(["bf16", "f16", "f32"]))
     causal = bool(r.integers(0, 2))
     window = None if r.random() < 0.6 else int(r.integers(0, 160))
     kl = None if r.random() < 0.5 else r.integers(0, Nk + 20, size=B).astype(np.int32)
     scale = float(np.float32([1.0 / np.sqrt(D), -0.07, 0.0, 0.3][int(r.integers(0, 4))]))
+    if large and window is not None:
+        window *= 8  # bands of up to ~1300 keys: several tiles wide
     return dict(B=B, H=H, Nq=Nq, Nk=Nk, D=D, dtype=dtype, causal=causal, window=window, kl=kl,
-                scale=scale, seed=9000 + i)
+                scale=scale, seed=(19000 if large else 9000) + i)
+
+
+@pytest.mark.parametrize("i", range(N_LARGE))
+def test_random_large_case(i, oracle_impl):
+    run_case(i, draw(i, large=True), oracle_impl)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_case(i, oracle_impl):
-    c = draw(i)
+    run_case(i, draw(i), oracle_impl)
+
+
+def run_case(i, c, oracle_impl):
     print(f"[random] case {i}: {c}", flush=True)
     w = inputs.Workload("r", c["dtype"], c["B"], c["H"], c["Nq"], c["Nk"], c["D"], c["causal"], False, 1.0, 1.0,
                        c["seed"])
