@@ -60,7 +60,7 @@ constexpr int NT = 256;    // threads per workgroup (4 waves)
 constexpr int BMQ = 128;   // dQ kernel: query rows per workgroup
 constexpr int BNQ = 64;    // dQ kernel: keys per K/V tile
 constexpr int BNK = 128;   // dK/dV kernel: keys per workgroup
-constexpr int BMK = 32;    // dK/dV kernel: query rows per Q/dO tile
+constexpr int BMK = 64;    // dK/dV kernel: query rows per Q/dO tile
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
 
@@ -448,88 +448,90 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
         const lds_u8* db = qb + TILE;
         const lds_u8* sb = qb + 2 * TILE;
 
-        // S = Q K^T, 32 queries x 32 keys per block.  Every row operand of S and dP is requested
-        // before the first product, so one wave per SIMD does not wait out the LDS latency per step.
-        static_assert(QB == 1, "one 32-row block per streamed tile");
-        u32x4_t qa[KSTEPS], da[KSTEPS];
+        // The tile is processed in 32-row blocks; a block none of whose rows reaches the wave's
+        // keys is skipped (a wave-uniform branch).
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) qa[ks] = *(const lds_u32x4*)(qb + raddr[ks]);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) da[ks] = *(const lds_u32x4*)(db + raddr[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16_t s[QB];
-        s[0] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) s[0] = M::mma(__builtin_bit_cast(vec8, qa[ks]), kf[ks], s[0]);
+        for (int qb2 = 0; qb2 < QB; ++qb2) {
+            const int ib = i0 + 32 * qb2;  // first row of the block
+            if (ib + 32 <= wave_row_lo || ib >= wave_row_hi) continue;
+            const lds_u8* qr = qb + qb2 * 32 * RB;
+            const lds_u8* dr = db + qb2 * 32 * RB;
 
-        // Exponent of P in base 2: scale S log2(e) - LSE log2(e), or -inf where a row cannot see
-        // the key.  Register i of s[qb2] holds query i0 + 32 qb2 + 16 (i/8) + 8 g + i%8; rows
-        // past Nq carry an LSE of +inf, so their weights are already 0.  The statistics of tile
-        // rows 32 qb2 + 16 (v4/2) + 8 g + 4 (v4%2) + 0..3 sit in one 16-byte LDS read each.
-        f32x4_t rs[QB][4];
-        float x[QB][16];
-        // the mask matters only if some key of the wave is padding or lies outside some row's range
-        const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > i0) ||
-                               (WIN && (i0 + BM - 1 - kw0 > p.window || kw0 + 31 - i0 > p.window));
+            // S = Q K^T, 32 queries x 32 keys.  Every row operand of S and dP is requested before
+            // the first product, so one wave per SIMD does not wait out the LDS latency per step.
+            u32x4_t qa[KSTEPS], da[KSTEPS];
 #pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2)
+            for (int ks = 0; ks < KSTEPS; ++ks) qa[ks] = *(const lds_u32x4*)(qr + raddr[ks]);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) da[ks] = *(const lds_u32x4*)(dr + raddr[ks]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16_t s = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) s = M::mma(__builtin_bit_cast(vec8, qa[ks]), kf[ks], s);
+
+            // Exponent of P in base 2: scale S log2(e) - LSE log2(e), or -inf where a row cannot
+            // see the key.  Register i of s holds query ib + 16 (i/8) + 8 g + i%8; rows past Nq
+            // carry an LSE of +inf, so their weights are already 0.  The statistics of block rows
+            // 16 (v4/2) + 8 g + 4 (v4%2) + 0..3 sit in one 16-byte LDS read each.
+            f32x4_t rs[4];
+            float x[16];
+            // the mask matters only if some key of the wave is padding or lies outside some row's range
+            const bool need_mask = kw0 + 31 >= kv_valid || (p.causal && kw0 + 31 > ib) ||
+                                   (WIN && (ib + 31 - kw0 > p.window || kw0 + 31 - ib > p.window));
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const int rl = 32 * qb2 + 16 * (v4 >> 1) + 8 * g + 4 * (v4 & 1);
                 const f32x4_t ls = *(const __attribute__((address_space(3))) f32x4_t*)(sb + rl * 4);
-                rs[qb2][v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + BM * 4 + rl * 4);
+                rs[v4] = *(const __attribute__((address_space(3))) f32x4_t*)(sb + BM * 4 + rl * 4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[qb2][4 * v4 + e] = __builtin_fmaf(s[qb2][4 * v4 + e], c2, -ls[e]);
+                for (int e = 0; e < 4; ++e) x[4 * v4 + e] = __builtin_fmaf(s[4 * v4 + e], c2, -ls[e]);
             }
-        if (need_mask) {
-#pragma unroll
-            for (int qb2 = 0; qb2 < QB; ++qb2)
+            if (need_mask) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int qrow = i0 + 32 * qb2 + 16 * (i >> 3) + 8 * g + (i & 7);
+                    const int qrow = ib + 16 * (i >> 3) + 8 * g + (i & 7);
                     const bool off = kj >= kv_valid || kj < attn::bwd_key_lo<WIN>(p, qrow) ||
                                      kj >= attn::bwd_key_hi<WIN>(p, qrow, kv_valid);
-                    x[qb2][i] = off ? -INFINITY : x[qb2][i];
+                    x[i] = off ? -INFINITY : x[i];
                 }
-        }
-
-        // From here on one straight-line block (the mask above only edits x): dP = dO V^T runs on
-        // the matrix cores while the exponentials form P, and dS of the second 16 rows forms under
-        // the dV / dK products of the first 16.
-        f32x16_t dp[QB];
-        dp[0] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) dp[0] = M::mma(__builtin_bit_cast(vec8, da[ks]), vf[ks], dp[0]);
-        // P = 2^x and dS = P (dP - Dr), rounded to T for the MFMAs
-        vec8 pb[2 * QB], dsb[2 * QB];
-#pragma unroll
-        for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(x[qb2][i]);
-                pb[2 * qb2 + (i >> 3)][i & 7] = (T)pv;
-                dsb[2 * qb2 + (i >> 3)][i & 7] = (T)(pv * (dp[qb2][i] - rs[qb2][i >> 2][i & 3]));
             }
 
-        // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+            // From here on one straight-line block (the mask above only edits x): dP = dO V^T runs
+            // on the matrix cores while the exponentials form P, and dS of the second 16 rows forms
+            // under the dV / dK products of the first 16.
+            f32x16_t dp = f32x16_t{};
 #pragma unroll
-        for (int h16 = 0; h16 < 2 * QB; ++h16) {
+            for (int ks = 0; ks < KSTEPS; ++ks) dp = M::mma(__builtin_bit_cast(vec8, da[ks]), vf[ks], dp);
+            // P = 2^x and dS = P (dP - Dr), rounded to T for the MFMAs
+            vec8 pb[2], dsb[2];
 #pragma unroll
-            for (int t = 0; t < DT; ++t) {
-                const s16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_lo[t] + 16 * h16 * RB));
-                const s16x4_t dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_hi[t] + 16 * h16 * RB));
-                const vec8 ad = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, dlo)[0],
-                                                                  __builtin_bit_cast(u32x2_t, dlo)[1],
-                                                                  __builtin_bit_cast(u32x2_t, dhi)[0],
-                                                                  __builtin_bit_cast(u32x2_t, dhi)[1]});
-                dva[t] = M::mma(ad, pb[h16], dva[t]);
-                const s16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_lo[t] + 16 * h16 * RB));
-                const s16x4_t qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_hi[t] + 16 * h16 * RB));
-                const vec8 aq = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, qlo)[0],
-                                                                  __builtin_bit_cast(u32x2_t, qlo)[1],
-                                                                  __builtin_bit_cast(u32x2_t, qhi)[0],
-                                                                  __builtin_bit_cast(u32x2_t, qhi)[1]});
-                dka[t] = M::mma(aq, dsb[h16], dka[t]);
+            for (int i = 0; i < 16; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(x[i]);
+                pb[i >> 3][i & 7] = (T)pv;
+                dsb[i >> 3][i & 7] = (T)(pv * (dp[i] - rs[i >> 2][i & 3]));
+            }
+
+            // dV^T += dO^T P and dK^T += Q^T dS, 16 queries per MFMA
+#pragma unroll
+            for (int h16 = 0; h16 < 2; ++h16) {
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const int ro = (32 * qb2 + 16 * h16) * RB;
+                    const s16x4_t dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_lo[t] + ro));
+                    const s16x4_t dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(db + taddr_hi[t] + ro));
+                    const vec8 ad = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, dlo)[0],
+                                                                      __builtin_bit_cast(u32x2_t, dlo)[1],
+                                                                      __builtin_bit_cast(u32x2_t, dhi)[0],
+                                                                      __builtin_bit_cast(u32x2_t, dhi)[1]});
+                    dva[t] = M::mma(ad, pb[h16], dva[t]);
+                    const s16x4_t qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_lo[t] + ro));
+                    const s16x4_t qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qb + taddr_hi[t] + ro));
+                    const vec8 aq = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, qlo)[0],
+                                                                      __builtin_bit_cast(u32x2_t, qlo)[1],
+                                                                      __builtin_bit_cast(u32x2_t, qhi)[0],
+                                                                      __builtin_bit_cast(u32x2_t, qhi)[1]});
+                    dka[t] = M::mma(aq, dsb[h16], dka[t]);
+                }
             }
         }
     };
