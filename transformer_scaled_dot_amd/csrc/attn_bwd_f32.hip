@@ -57,7 +57,7 @@ __global__ void __launch_bounds__(64 * NWB) attn_bwd_f32_dq_kernel(attn::BwdPara
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_q);
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_q, p.n_qtiles);
     const int bh = blk / p.n_qtiles;
     int qt = blk - bh * p.n_qtiles;
     if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(64 * NWB) attn_bwd_f32_dkdv_kernel(attn::BwdPa
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kk = lane >> 2, part = lane & 3;  // key within the tile, quarter of the columns
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_k);
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_k, p.n_ktiles);
     const int bh = blk / p.n_ktiles;
     const int kt_idx = blk - bh * p.n_ktiles;
     const int b = bh / p.H;

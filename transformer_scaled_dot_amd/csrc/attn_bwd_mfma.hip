@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(attn::BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_q);
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_q, p.n_qtiles);
     const int bh = blk / p.n_qtiles;
     int qt = blk - bh * p.n_qtiles;
     if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(attn::BwdParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
-    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_k);
+    const int blk = attn::xcd_remap(blockIdx.x, p.n_blocks_k, p.n_ktiles);
     const int bh = blk / p.n_ktiles;
     const int kt_idx = blk - bh * p.n_ktiles;
     const int b = bh / p.H;

@@ -59,11 +59,21 @@ __device__ __forceinline__ int row_key_hi(const Params& p, int i, int kv_valid) 
     return hi;
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).
-// Renumber them so that each XCD walks one contiguous range of the logical order: the
-// q-tiles of one (b, h) then run on the same XCD at about the same time and share the K/V
-// stream through that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).  In the
+// logical order every `group` consecutive items share one (b, h), and with it the stream of K/V
+// (or Q/dO) tiles.  Whole groups are dealt round-robin over the XCDs: XCD x walks groups x, x + 8,
+// x + 16, ... in turn, each group's items back to back, so that a group runs on one XCD at about
+// the same time and shares that XCD's L2, while groups of unequal work (padded or ragged sequence
+// lengths, which vary with b) spread evenly over the XCDs instead of one XCD taking a run of whole
+// batches.  With a group count that is not a multiple of 8, each XCD walks one contiguous range of
+// the logical order (or the identity order when n itself is not a multiple of 8).  n must be a
+// multiple of group.
+__device__ __forceinline__ int xcd_remap(int bid, int n, int group) {
+    if (((n / group) & 7) == 0) {
+        const int x = bid & 7, k = bid >> 3;
+        const int gi = k / group, within = k - gi * group;
+        return ((gi << 3) + x) * group + within;
+    }
     if ((n & 7) != 0) return bid;
     return (bid & 7) * (n >> 3) + (bid >> 3);
 }

@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
-    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks));
+    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits));
     const int bh = bw.bh;
     int qt = bw.qt;
     if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;  // longest rows first
