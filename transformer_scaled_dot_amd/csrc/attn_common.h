@@ -37,7 +37,7 @@ struct Params {
 struct BlockWork {
     int split, bh, qt;
 };
-__device__ __forceinline__ BlockWork block_work(const Params& p, int blk) {
+__host__ __device__ __forceinline__ BlockWork block_work(const Params& p, int blk) {
     BlockWork w;
     w.split = blk % p.n_splits;
     const int rest = blk / p.n_splits;
@@ -68,7 +68,7 @@ __device__ __forceinline__ int row_key_hi(const Params& p, int i, int kv_valid) 
 // batches.  With a group count that is not a multiple of 8, each XCD walks one contiguous range of
 // the logical order (or the identity order when n itself is not a multiple of 8).  n must be a
 // multiple of group.
-__device__ __forceinline__ int xcd_remap(int bid, int n, int group) {
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n, int group) {
     if (((n / group) & 7) == 0) {
         const int x = bid & 7, k = bid >> 3;
         const int gi = k / group, within = k - gi * group;
