@@ -51,16 +51,18 @@ typedef enum {
 } attn_dtype;
 
 typedef enum {
+    /* The first seven codes and their values are the interface's original set. */
     ATTN_OK = 0,
-    ATTN_ERR_NULL = -1,     /* q, k, v, o or lse is NULL */
-    ATTN_ERR_SHAPE = -2,    /* B, H, Nq or Nk < 1, or a size beyond the 32-bit limits below */
-    ATTN_ERR_HEAD_DIM = -3, /* D is not 64 or 128 */
-    ATTN_ERR_DTYPE = -4,    /* dtype is not an attn_dtype (attn_bwd: not ATTN_F16 / ATTN_BF16) */
-    ATTN_ERR_SCALE = -5,    /* scale is not finite */
-    ATTN_ERR_FLAG = -6,     /* causal is not 0 or 1 */
-    ATTN_ERR_LAUNCH = -7,   /* the HIP runtime rejected the kernel launch */
-    ATTN_ERR_ALIGN = -8,    /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
-    ATTN_ERR_WINDOW = -9,   /* window is below -1 (attn_fwd_window) */
+    ATTN_ERR_NULL = -1,      /* q, k, v, o or lse is NULL (attn_decode, attn_bwd: also a needed workspace) */
+    ATTN_ERR_SHAPE = -2,     /* B, H, Nq or Nk < 1, or a size beyond the 32-bit limits below */
+    ATTN_ERR_HEAD_DIM = -3,  /* D is not 64 or 128 */
+    ATTN_ERR_DTYPE = -4,     /* dtype is not an attn_dtype */
+    ATTN_ERR_SCALE = -5,     /* scale is not finite */
+    ATTN_ERR_LAUNCH = -6,    /* the HIP runtime rejected the kernel launch */
+    /* Added after the original set, which had no code for these argument errors. */
+    ATTN_ERR_FLAG = -7,      /* causal is not 0 or 1 */
+    ATTN_ERR_ALIGN = -8,     /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
+    ATTN_ERR_WINDOW = -9,    /* window is below -1 (attn_fwd_window, attn_bwd_window) */
     ATTN_ERR_WORKSPACE = -10 /* workspace smaller than the *_workspace_size() query (attn_decode, attn_bwd) */
 } attn_status;
 

@@ -7,8 +7,10 @@
  *            [B, H, Nq, D] then [B, H, Nk, D] twice, row-major
  *   out.bin  o ([B, H, Nq, D], storage bytes of `dtype`) then lse (fp32 [B, H, Nq])
  * The scale is 1/sqrt(D).  Device memory comes from the HIP runtime (the library allocates
- * nothing); the call runs on a stream the program creates.  It also makes one call with an
- * unsupported head dimension and checks that it is refused with ATTN_ERR_HEAD_DIM.
+ * nothing); the call runs on a stream the program creates.  It also makes calls that must be
+ * refused on the host, one from each group of status codes: an unsupported head dimension
+ * (ATTN_ERR_HEAD_DIM, of the original set) and a causal flag of 2 (ATTN_ERR_FLAG, added later),
+ * and checks the codes by their names and values.
  * Exit status 0 on success.
  */
 #include <math.h>
@@ -49,10 +51,14 @@ int main(int argc, char** argv) {
         hipMemcpy(v, host + (nq + nk) * es, nk * es, hipMemcpyHostToDevice))
         return fail("copy to the device");
 
-    /* an unsupported head dimension is refused on the host, before anything is enqueued */
+    /* bad arguments are refused on the host, before anything is enqueued */
     const int bad = attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, 96, 0.1f, causal, NULL, dtype, stream);
-    if (bad != ATTN_ERR_HEAD_DIM) return fail("D = 96 was not refused");
+    if (bad != ATTN_ERR_HEAD_DIM || ATTN_ERR_HEAD_DIM != -3) return fail("D = 96 was not refused with -3");
     printf("D=96: %s\n", attn_status_str(bad));
+    const int bad_flag = attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, 0.1f, 2, NULL, dtype, stream);
+    if (bad_flag != ATTN_ERR_FLAG || ATTN_ERR_FLAG != -7) return fail("causal = 2 was not refused with -7");
+    printf("causal=2: %s\n", attn_status_str(bad_flag));
+    if (ATTN_ERR_LAUNCH != -6) return fail("ATTN_ERR_LAUNCH is not -6");
 
     const int rc = attn_fwd(q, k, v, o, lse, B, H, Nq, Nk, D, (float)(1.0 / sqrt((double)D)), causal, NULL,
                             dtype, stream);

@@ -42,6 +42,26 @@ def test_library_exports_every_declared_symbol():
     assert exported == set(declared_functions()), f"unexpected exports: {sorted(exported - set(declared_functions()))}"
 
 
+def header_status_codes():
+    """The attn_status enum as include/attn_fwd.h declares it: {name: value}."""
+    text = open(os.path.join(INCLUDE, "attn_fwd.h")).read()
+    body = re.search(r"typedef enum \{([^{}]*)\} attn_status;", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(ATTN_\w+)\s*=\s*(-?\d+)", body)}
+
+
+def test_status_codes_pinned():
+    """The seven codes of the interface's original set keep their values (a caller built against
+    it reads them unchanged); the codes added later follow from -7 down; the binding mirrors the
+    header exactly."""
+    codes = header_status_codes()
+    original = {"ATTN_OK": 0, "ATTN_ERR_NULL": -1, "ATTN_ERR_SHAPE": -2, "ATTN_ERR_HEAD_DIM": -3,
+                "ATTN_ERR_DTYPE": -4, "ATTN_ERR_SCALE": -5, "ATTN_ERR_LAUNCH": -6}
+    added = {"ATTN_ERR_FLAG": -7, "ATTN_ERR_ALIGN": -8, "ATTN_ERR_WINDOW": -9, "ATTN_ERR_WORKSPACE": -10}
+    assert codes == {**original, **added}
+    assert {v: k for k, v in codes.items()} == binding.STATUS
+
+
 def test_status_strings():
     for code in binding.STATUS:
         s = binding.attn_status_str(code)
@@ -56,7 +76,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
     (dict(q=None), -1), (dict(lse=None), -1), (dict(B=0), -2), (dict(H=-1), -2),
     (dict(Nq=0), -2), (dict(Nk=0), -2), (dict(D=32), -3), (dict(D=256), -3), (dict(dtype=3), -4),
     (dict(dtype=-1), -4), (dict(scale=float("nan")), -5), (dict(scale=float("-inf")), -5),
-    (dict(causal=-1), -6), (dict(causal=2), -6), (dict(Nk=1 << 23, D=64), -2),
+    (dict(causal=-1), -7), (dict(causal=2), -7), (dict(Nk=1 << 23, D=64), -2),
     (dict(o=FAKE + 8), -8), (dict(q=FAKE + 2), -8), (dict(key_lens=FAKE + 2), -8),
 ])
 def test_host_validation(over, code):
@@ -71,7 +91,7 @@ def test_host_validation(over, code):
 
 @pytest.mark.parametrize("over,code", [
     (dict(window=-2), -9), (dict(window=-(1 << 30)), -9), (dict(q=None), -1), (dict(D=32), -3),
-    (dict(causal=2), -6), (dict(o=FAKE + 8), -8), (dict(window=-2, causal=3), -6),
+    (dict(causal=2), -7), (dict(o=FAKE + 8), -8), (dict(window=-2, causal=3), -7),
 ])
 def test_host_validation_window(over, code):
     """attn_fwd_window checks its band argument on the host like the others."""
@@ -107,7 +127,7 @@ DECODE_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, Nq=1, Nk=40
 
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), -1), (dict(B=0), -2), (dict(D=96), -3), (dict(dtype=5), -4),
-    (dict(scale=float("inf")), -5), (dict(causal=2), -6), (dict(lse=FAKE + 4), -8),
+    (dict(scale=float("inf")), -5), (dict(causal=2), -7), (dict(lse=FAKE + 4), -8),
     (dict(ws=None), -1), (dict(ws=FAKE + 8), -8), (dict(ws_bytes=0), -10), (dict(ws_bytes=4159), -10),
 ])
 def test_host_validation_decode(over, code):
@@ -149,7 +169,7 @@ BWD_OK = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dlse=None, dq=F
 @pytest.mark.parametrize("over,code", [
     (dict(q=None), -1), (dict(do=None), -1), (dict(dv=None), -1), (dict(lse=None), -1),
     (dict(B=0), -2), (dict(Nk=0), -2), (dict(D=96), -3), (dict(dtype=-1), -4), (dict(dtype=3), -4),
-    (dict(scale=float("nan")), -5), (dict(causal=2), -6), (dict(dq=FAKE + 4), -8),
+    (dict(scale=float("nan")), -5), (dict(causal=2), -7), (dict(dq=FAKE + 4), -8),
     (dict(dlse=FAKE + 4), -8), (dict(key_lens=FAKE + 1), -8), (dict(ws=None), -1),
     (dict(ws=FAKE + 8), -8), (dict(ws_bytes=2 * 2 * 3 * 64 * 4 - 1), -10), (dict(Nq=1 << 22, D=128), -2),
     (dict(B=4096, H=64, Nq=1024, D=64, ws_bytes=1 << 40), -2),
@@ -176,7 +196,7 @@ def test_bwd_workspace_size():
 
 @pytest.mark.parametrize("over,code", [
     (dict(window=-2), -9), (dict(window=-1000), -9), (dict(q=None), -1), (dict(dtype=3), -4),
-    (dict(causal=2), -6), (dict(ws=None), -1),
+    (dict(causal=2), -7), (dict(ws=None), -1),
 ])
 def test_host_validation_bwd_window(over, code):
     """attn_bwd_window checks its band argument on the host like the others."""

@@ -36,7 +36,7 @@ def test_c_caller_matches_oracle(dtype, D, causal, tmp_path, oracle_impl):
     r = subprocess.run(args, capture_output=True, text=True, timeout=120)
     print(r.stdout, r.stderr, flush=True)
     assert r.returncode == 0
-    assert "D=96: " in r.stdout and "attn_fwd: " in r.stdout
+    assert "D=96: " in r.stdout and "causal=2: " in r.stdout and "attn_fwd: " in r.stdout
     raw = np.fromfile(dst, dtype=np.uint8)
     n_o = w.B * w.H * w.Nq * D
     store = x["q"].dtype

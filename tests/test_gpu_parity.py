@@ -61,6 +61,38 @@ def test_parity_sampled_rows_full_size(name, oracle_impl):
     assert torch.equal(o[:, :, 0], v0)
 
 
+def test_parity_every_row_decoder_4k(oracle_impl):
+    """The 4K causal workload (B=4, H=32, D=128) at full size, in the benchmark's launch
+    configuration: every one of its 524,288 rows against the oracle."""
+    name = "decoder_causal_bf16_b4h32n4096d128"
+    w = inputs.WORKLOADS[name]
+    log(f"[parity] {name} (every row)")
+    x = inputs.make_inputs(w)
+    o, lse = run(x, w.dtype, w.causal)
+    ro, rl = oracle_impl.attn(x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), w.causal, x["key_lens"])
+    eo, el = compare(o, lse, ro, rl, w.dtype, name)
+    log(f"[parity] {name}: all {w.B * w.H * w.Nq} rows, max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+
+
+def test_parity_longctx_16k_whole_heads_and_random_rows(oracle_impl):
+    """The 16K causal workload (B=1, H=32, D=128) at full size: every row of two whole heads (the
+    first and the last, 32,768 rows) plus 65,536 rows drawn at random from the other heads."""
+    name = "longctx_causal_bf16_b1h32n16384d128"
+    w = inputs.WORKLOADS[name]
+    log(f"[parity] {name} (two whole heads + 65536 random rows)")
+    x = inputs.make_inputs(w)
+    o, lse = run(x, w.dtype, w.causal)
+    heads = [0, w.B * w.H - 1]
+    whole = np.concatenate([np.arange(h * w.Nq, (h + 1) * w.Nq, dtype=np.int64) for h in heads])
+    rng = np.random.default_rng(2024)
+    others = rng.choice(np.arange(w.Nq, (w.B * w.H - 1) * w.Nq, dtype=np.int64), size=65536, replace=False)
+    rows = np.unique(np.concatenate([whole, others]))
+    ro, rl = oracle_impl.attn_rows(x["q"], x["k"], x["v"], w.dtype, float(x["scale"]), w.causal,
+                                   x["key_lens"], rows)
+    eo, el = compare(o, lse, ro, rl, w.dtype, name, rows=rows)
+    log(f"[parity] {name}: {rows.size} rows, max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # name, B, H, Nq, Nk, D, causal, key_lens, scale
@@ -253,7 +285,7 @@ def test_invalid_arguments_write_nothing():
         (dict(dtype=9), -4),
         (dict(scale=float("nan")), -5),
         (dict(scale=float("inf")), -5),
-        (dict(causal=2), -6),
+        (dict(causal=2), -7),
         (dict(Nq=(1 << 29) // 64), -2),
     ]
     for over, code in bad:

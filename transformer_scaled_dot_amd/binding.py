@@ -23,7 +23,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 ATTN_OK = 0
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
-    -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_FLAG", -7: "ATTN_ERR_LAUNCH",
+    -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_LAUNCH", -7: "ATTN_ERR_FLAG",
     -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE",
 }
 EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size",
