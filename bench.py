@@ -514,7 +514,29 @@ def main():
             f"sample max|dO|={cb['sample_max_abs_err_o']:.3e} max|dLSE|={cb['sample_max_abs_err_lse']:.3e}")
     else:
         result["cpu_baseline"] = None
+    # The CPU baseline's sample doubles as a parity check at the benchmarked size and launch
+    # configuration: the line is printed either way, and the run fails if the sample breaks the
+    # tolerance (O: 2e-2 for bf16/fp16, 1e-4 for fp32; LSE: 1e-3; backward: each gradient's max
+    # error within 2e-2 (1e-4 for fp32) of its largest entry).
+    parity_ok = True
+    cb = result["cpu_baseline"]
+    if cb is not None:
+        tol_o = 1e-4 if w.dtype == "f32" else 2e-2
+        if bwd:
+            parity_ok = cb["sample_max_rel_err_grads"] <= tol_o
+            result["parity"] = {"checked": cb["sample"].split(" random")[0] + " (b, h) slices",
+                                "max_rel_err_grads": cb["sample_max_rel_err_grads"], "tol": tol_o,
+                                "pass": parity_ok}
+        else:
+            parity_ok = cb["sample_max_abs_err_o"] <= tol_o and cb["sample_max_abs_err_lse"] <= 1e-3
+            result["parity"] = {"checked": cb["sample"].split(" random")[0] + " rows",
+                                "max_abs_err_o": cb["sample_max_abs_err_o"], "tol_o": tol_o,
+                                "max_abs_err_lse": cb["sample_max_abs_err_lse"], "tol_lse": 1e-3,
+                                "pass": parity_ok}
     print(json.dumps(result), flush=True)
+    if not parity_ok:
+        log(f"[bench] PARITY FAILURE against the oracle on the sampled rows: {result['parity']}")
+        sys.exit(1)
 
 
 if __name__ == "__main__":
