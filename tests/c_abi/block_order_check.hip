@@ -7,7 +7,7 @@
 
 #include "attn_common.h"
 
-static int check(int B, int H, int n_qtiles, int n_splits) {
+static int check(int B, int H, int n_qtiles, int n_splits, int inter) {
     attn::Params p{};
     p.B = B;
     p.H = H;
@@ -17,7 +17,7 @@ static int check(int B, int H, int n_qtiles, int n_splits) {
     const int n = group * B * H;
     std::vector<int> seen_id(n, 0), seen_work(n, 0);
     for (int bid = 0; bid < n; ++bid) {
-        const int blk = attn::xcd_remap(bid, n, group);
+        const int blk = attn::xcd_remap(bid, n, group, inter);
         if (blk < 0 || blk >= n || seen_id[blk]++) return 1;
         const attn::BlockWork w = attn::block_work(p, blk);
         if (w.split < 0 || w.split >= n_splits || w.bh < 0 || w.bh >= B * H || w.qt < 0 || w.qt >= n_qtiles)
@@ -31,18 +31,19 @@ static int check(int B, int H, int n_qtiles, int n_splits) {
 
 int main() {
     const int Bs[] = {1, 2, 3, 4, 16, 32}, Hs[] = {1, 2, 8, 12, 32}, Qs[] = {1, 2, 3, 4, 32, 128},
-              Ss[] = {1, 2, 5, 64};
+              Ss[] = {1, 2, 5, 64}, Ps[] = {1, 2, 3, 4};
     int cases = 0;
     for (int B : Bs)
         for (int H : Hs)
             for (int Q : Qs)
-                for (int S : Ss) {
-                    ++cases;
-                    if (check(B, H, Q, S)) {
-                        printf("FAIL B=%d H=%d n_qtiles=%d n_splits=%d\n", B, H, Q, S);
-                        return 1;
+                for (int S : Ss)
+                    for (int P : Ps) {
+                        ++cases;
+                        if (check(B, H, Q, S, P)) {
+                            printf("FAIL B=%d H=%d n_qtiles=%d n_splits=%d interleave=%d\n", B, H, Q, S, P);
+                            return 1;
+                        }
                     }
-                }
     printf("ok %d\n", cases);
     return 0;
 }

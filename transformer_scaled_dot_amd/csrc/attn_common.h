@@ -22,6 +22,7 @@ struct Params {
     int causal;
     int causal_br;     // causal mask aligned bottom-right: query i keeps keys j <= i + L_b - Nq
     int window;        // half-width w of the local band |i - j| <= w, or -1 for none
+    int xcd_interleave;  // groups each XCD alternates between (xcd_remap); 1 = one at a time
     // Key-range split: each (Q tile, b, h) is spread over n_splits workgroups, split s taking
     // keys [s * split_len, (s + 1) * split_len).  With n_splits > 1 the workgroups write fp32
     // partial results (O normalised over the split's keys, LSE of the split) to o_part
@@ -62,15 +63,25 @@ __device__ __forceinline__ int row_key_hi(const Params& p, int i, int kv_valid) 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on XCD i % 8).  In the
 // logical order every `group` consecutive items share one (b, h), and with it the stream of K/V
 // (or Q/dO) tiles.  Whole groups are dealt round-robin over the XCDs: XCD x walks groups x, x + 8,
-// x + 16, ... in turn, each group's items back to back, so that a group runs on one XCD at about
-// the same time and shares that XCD's L2, while groups of unequal work (padded or ragged sequence
-// lengths, which vary with b) spread evenly over the XCDs instead of one XCD taking a run of whole
-// batches.  With a group count that is not a multiple of 8, each XCD walks one contiguous range of
-// the logical order (or the identity order when n itself is not a multiple of 8).  n must be a
-// multiple of group.
-__host__ __device__ __forceinline__ int xcd_remap(int bid, int n, int group) {
+// x + 16, ... in turn, so that a group runs on one XCD at about the same time and shares that
+// XCD's L2, while groups of unequal work (padded or ragged sequence lengths, which vary with b)
+// spread evenly over the XCDs instead of one XCD taking a run of whole batches.  With
+// `interleave` = P > 1 (P dividing the XCD's group count), the XCD walks its groups P at a time
+// and alternates between them item by item: with causal Q tiles ordered longest first inside a
+// group, the XCD then starts the P longest tiles of P heads before any shorter one, and the
+// shortest tiles of the last heads fill the end instead of a few long ones running alone.  With a
+// group count that is not a multiple of 8, each XCD walks one contiguous range of the logical
+// order (or the identity order when n itself is not a multiple of 8).  n must be a multiple of
+// group.
+__host__ __device__ __forceinline__ int xcd_remap(int bid, int n, int group, int interleave = 1) {
     if (((n / group) & 7) == 0) {
         const int x = bid & 7, k = bid >> 3;
+        const int P = interleave;
+        if (P > 1 && ((n / group / 8) % P) == 0) {
+            const int chunk = k / (P * group), w = k - chunk * P * group;
+            const int item = w / P, sub = w - item * P;
+            return (((chunk * P + sub) << 3) + x) * group + item;
+        }
         const int gi = k / group, within = k - gi * group;
         return ((gi << 3) + x) * group + within;
     }

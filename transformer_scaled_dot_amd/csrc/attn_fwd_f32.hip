@@ -33,7 +33,7 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits));
+    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits, p.xcd_interleave));
     const int bh = bw.bh;
     int qt = bw.qt;
     if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;

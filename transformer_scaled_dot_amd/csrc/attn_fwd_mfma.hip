@@ -7,7 +7,8 @@
 //   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
 //   * K/V tiles of 64 keys go HBM -> LDS by the buffer-load-to-LDS path (no registers, no LDS
 //     store instructions), double buffered, one barrier per tile; the next tile's loads are in
-//     flight while the current one is computed;
+//     flight while the current one is computed.  The copies are issued as assembly and waited
+//     for explicitly, so that no LDS read of the current tile waits for the next tile's copy;
 //   * both products run on v_mfma_f32_32x32x16_{bf16,f16} with fp32 accumulation, arranged so
 //     that a lane always holds one query row:
 //        S^T = K Q^T   (A = K tile read from LDS, B = Q^T kept in registers for the whole loop)
@@ -88,6 +89,29 @@ __device__ __forceinline__ int vswz_row(int row) {
     return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+// One 16-byte-per-lane copy HBM -> LDS (buffer load to LDS): lane l's 16 bytes from byte offset
+// voff + soff of the buffer land at LDS byte address lds_base + 16 l.  The compiler cannot tell
+// which LDS bytes such a copy writes; issued through its builtin, every later LDS read (the V^T
+// transpose reads of the current tile in particular) would wait for all copies in flight,
+// including the next tile's.  Issued as assembly it is invisible to that bookkeeping, and the
+// kernel waits for its own copies (vmcnt) before the barrier that publishes a tile.  The
+// instruction writes no registers; m0 carries the LDS address.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t rsrc, unsigned lds_base, int voff,
+                                            int soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_base)
+                 : "memory");
+}
+
+// The lane id (0..63), computed where it is used: the volatile assembly has no inputs, so the
+// compiler cannot hoist it and keep it in a register for the length of the loop.
+__device__ __forceinline__ int lane_id_here() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 template <typename T, int D>
 __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     // The body is device code only: its LDS address-space casts mean nothing to the host pass,
@@ -113,7 +137,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, g = lane >> 5;
 
-    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits));
+    const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits, p.xcd_interleave));
     const int bh = bw.bh;
     int qt = bw.qt;
     if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;  // longest rows first
@@ -151,15 +175,16 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
     const int n_tiles = (kv_end + BN - 1) / BN;
     const int t_begin = k_begin / BN;
 
-    // Per-lane byte offsets of this thread's tile loads: slot (i*NT + tid) of a tile holds the
-    // global 16-byte chunk (row, chunk ^ swizzle(row)).
-    int koff[CPT], voff[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int s = i * NT + tid;
-        const int row = s / NCH, phys = s % NCH;
-        koff[i] = (row * D + (phys ^ kswz_row<D>(row)) * 8) * 2;
-        voff[i] = (row * D + (phys ^ vswz_row<D>(row)) * 8) * 2;
+    // This thread's 16-byte copy slots of a tile are i NT + tid (i < CPT): row (i NT + tid) / NCH,
+    // chunk (tid % NCH) ^ swizzle(row).  The swizzles depend on the row only modulo 16 (K, D = 128),
+    // 32 (K, D = 64) and 4 (V), and NT / NCH (16 or 32) rows separate consecutive slots, so slot i
+    // sits i NT 16 bytes after slot 0 (a scalar offset) with the same chunk order.
+    static_assert(NT / NCH == 16 || NT / NCH == 32, "copy slots must share their swizzle");
+    int koff0, voff0;
+    {
+        const unsigned row = (unsigned)tid / NCH, phys = (unsigned)tid % NCH;
+        koff0 = (int)((row * D + (phys ^ kswz_row<D>(row)) * 8) * 2);
+        voff0 = (int)((row * D + (phys ^ vswz_row<D>(row)) * 8) * 2);
     }
     auto issue_tile = [&](const int tile, const int stage) {
         const int j0 = tile * BN;
@@ -171,34 +196,32 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
             __builtin_amdgcn_make_buffer_rsrc((void*)(vg + (size_t)j0 * D), 0, bytes, kBufferWord3);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            lds_u8* kd = smem + stage * STAGE + (i * NT + wave * 64) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)kd, 16, koff[i], 0, 0, 0);
+            const unsigned kd = __builtin_amdgcn_readfirstlane(
+                (unsigned)(uintptr_t)(smem + stage * STAGE + (i * NT + wave * 64) * 16));
+            copy_to_lds(krs, kd, koff0, i * NT * 16);
         }
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            lds_u8* vd = smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)vd, 16, voff[i], 0, 0, 0);
+            const unsigned vd = __builtin_amdgcn_readfirstlane(
+                (unsigned)(uintptr_t)(smem + stage * STAGE + TILE + (i * NT + wave * 64) * 16));
+            copy_to_lds(vrs, vd, voff0, i * NT * 16);
         }
     };
 
     // Per-lane LDS read offsets.
-    // K (A operand of S^T): row swap23(r) (+32 kt), chunk (2 ks + g) ^ kswz.
-    int kaddr[KSTEPS];
-    {
-        const int kr = kswz_lane<D>(r);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) kaddr[ks] = swap23(r) * (D * 2) + (((2 * ks + g) ^ kr) * 16);
-    }
+    // K (A operand of S^T) at k-step ks: row swap23(r) (+32 kt), chunk (2 ks + g) ^ kswz.  Chunk
+    // bit 0 is g ^ (kswz & 1) and the upper chunk bits are ks ^ (kswz >> 1), so k-step ks reads at
+    // kbase ^ (32 ks): one register and one XOR per read instead of a register per k-step.
+    const int kbase = swap23(r) * (D * 2) + ((g ^ (kswz_lane<D>(r) & 1)) * 16) + (kswz_lane<D>(r) >> 1) * 32;
     // V^T (A operand of O^T) by transpose reads: within each 16-lane group (s = lane & 15), lane
     // s names 8 bytes of V row (16 h16 + 8 g + 4 u + s/4) at columns 32 dt + 16 G + 4 (s & 3);
-    // lane s then receives column 32 dt + 16 G + s of those 4 rows.
-    int vaddr[DT];
+    // lane s then receives column 32 dt + 16 G + s of those 4 rows.  Column tile dt sits at
+    // vbase ^ (64 dt).
+    int vbase;
     {
         const int s = lane & 15, G1 = (lane >> 4) & 1;
         const int fl = vswz_row<D>(s >> 2) >> 2;  // rows of one read differ only in their low 2 bits
-        const int base = (8 * g + (s >> 2)) * (D * 2) + (2 * G1 + ((s & 3) >> 1)) * 16 + 8 * (s & 1);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vaddr[dt] = base + 64 * (dt ^ fl);
+        vbase = (8 * g + (s >> 2)) * (D * 2) + (2 * G1 + ((s & 3) >> 1)) * 16 + 8 * (s & 1) + 64 * fl;
     }
 
     f32x16_t oacc[DT];
@@ -231,7 +254,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
             s[kt] = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const u32x4_t a = *(const lds_u32x4*)(kb + kaddr[ks] + kt * 32 * D * 2);
+                const u32x4_t a = *(const lds_u32x4*)(kb + (kbase ^ (32 * ks)) + kt * 32 * D * 2);
                 s[kt] = M::mma(__builtin_bit_cast(vec8, a), qf[ks], s[kt]);
             }
         }
@@ -242,14 +265,21 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
                                j0 < attn::row_key_lo(p, qw0 + 31);
         float mt;
         if (need_mask) {
-            const int lo = attn::row_key_lo(p, qi), hi = attn::row_key_hi(p, qi, kv_valid);
+            // Register i holds key j0 + 8 g + kk with kk = 32 kt + 16 (i / 8) + i % 8 a constant;
+            // it is visible iff kk - lo' lies in [0, hi - lo), lo' = lo - j0 - 8 g: one unsigned
+            // compare per element.  The lane id is recomputed here rather than kept live.
+            const int l = lane_id_here();
+            const int row = qw0 + (l & 31);
+            const int lo = attn::row_key_lo(p, row), hi = attn::row_key_hi(p, row, kv_valid);
+            const int lo_rel = lo - j0 - 8 * (l >> 5);
+            const unsigned span = hi > lo ? (unsigned)(hi - lo) : 0u;
             mt = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int j = j0 + 32 * kt + 16 * (i >> 3) + 8 * g + (i & 7);
-                    const float t = (j >= lo && j < hi) ? s[kt][i] * c2 : -INFINITY;
+                    const int kk = 32 * kt + 16 * (i >> 3) + (i & 7);
+                    const float t = (unsigned)(kk - lo_rel) < span ? s[kt][i] * c2 : -INFINITY;
                     s[kt][i] = t;
                     mt = fmaxf(mt, t);
                 }
@@ -306,7 +336,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         for (int h16 = 0; h16 < BN / 16; ++h16) {
 #pragma unroll
             for (int t = 0; t < DT; ++t) {
-                const lds_u8* a0 = vb + vaddr[t] + (16 * h16) * (D * 2);
+                const lds_u8* a0 = vb + (vbase ^ (64 * t)) + (16 * h16) * (D * 2);
                 const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a0);
                 const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 4 * D * 2));
                 const vec8 a = __builtin_bit_cast(vec8, u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0],
