@@ -63,7 +63,8 @@ typedef enum {
     ATTN_ERR_FLAG = -7,      /* causal is not 0 or 1 */
     ATTN_ERR_ALIGN = -8,     /* q, k, v, o or lse is not 16-byte aligned (key_lens: 4-byte) */
     ATTN_ERR_WINDOW = -9,    /* window is below -1 (attn_fwd_window, attn_bwd_window) */
-    ATTN_ERR_WORKSPACE = -10 /* workspace smaller than the *_workspace_size() query (attn_decode, attn_bwd) */
+    ATTN_ERR_WORKSPACE = -10, /* workspace smaller than the *_workspace_size() query (attn_decode, attn_bwd) */
+    ATTN_ERR_SCRATCH = -11    /* attn_decode_noalloc: the call needs more than ATTN_DECODE_SCRATCH_BYTES */
 } attn_status;
 
 /*
@@ -149,6 +150,33 @@ ATTN_API int attn_decode(const void* q, const void* k, const void* v, void* o, f
  * needs none, or when the sizes are invalid).  A pure function of its arguments.
  */
 ATTN_API size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D, int dtype);
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the split partials
+ * go to a scratch buffer the library holds itself, a static device array of
+ * ATTN_DECODE_SCRATCH_BYTES per GPU (reserved on each GPU the library runs on, until the process
+ * ends).  Nothing is allocated, here or in the call: no hipMalloc, no hipFree, no allocating
+ * library routine.  The first call on a device looks up that device's copy of the array.
+ *
+ *   arguments   as attn_decode without the workspace; results are bitwise those of
+ *               attn_decode for the same inputs.
+ *   limit       the call needs attn_decode_workspace_size(B, H, Nq, Nk, D, dtype) bytes of
+ *               scratch; above ATTN_DECODE_SCRATCH_BYTES it returns ATTN_ERR_SCRATCH and enqueues
+ *               nothing (use attn_decode with a workspace then).  With one query per sequence
+ *               the need is about 0.5 MiB for any batch; it grows with Nq (about 16 MiB at
+ *               Nq = 31, D = 128).
+ *   concurrency every call on one GPU shares that GPU's scratch: calls that overlap in time on
+ *               one GPU (different streams, different host threads) race and must not be made.
+ *               Nothing in the scratch needs clearing between calls (each call overwrites what
+ *               it reads).
+ * Errors as attn_decode, plus ATTN_ERR_SCRATCH; ATTN_ERR_LAUNCH if the scratch's device address
+ * cannot be obtained on the current device.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+ATTN_API int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                 int H, int Nq, int Nk, int D, float scale, int causal,
+                                 const int32_t* key_lens, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 ATTN_API const char* attn_status_str(int status);

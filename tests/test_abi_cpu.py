@@ -57,7 +57,8 @@ def test_status_codes_pinned():
     codes = header_status_codes()
     original = {"ATTN_OK": 0, "ATTN_ERR_NULL": -1, "ATTN_ERR_SHAPE": -2, "ATTN_ERR_HEAD_DIM": -3,
                 "ATTN_ERR_DTYPE": -4, "ATTN_ERR_SCALE": -5, "ATTN_ERR_LAUNCH": -6}
-    added = {"ATTN_ERR_FLAG": -7, "ATTN_ERR_ALIGN": -8, "ATTN_ERR_WINDOW": -9, "ATTN_ERR_WORKSPACE": -10}
+    added = {"ATTN_ERR_FLAG": -7, "ATTN_ERR_ALIGN": -8, "ATTN_ERR_WINDOW": -9, "ATTN_ERR_WORKSPACE": -10,
+             "ATTN_ERR_SCRATCH": -11}
     assert codes == {**original, **added}
     assert {v: k for k, v in codes.items()} == binding.STATUS
 
@@ -217,3 +218,34 @@ def test_c_caller_is_built_and_checks_its_arguments():
     assert os.access(caller, os.X_OK)
     r = subprocess.run([caller], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), -1), (dict(D=96), -3), (dict(causal=2), -7), (dict(o=FAKE + 8), -8),
+    # B=1, H=32, Nq=128, Nk=16384, D=128: 32 key splits of 128 rows need 67.6 MB of partials
+    (dict(B=1, H=32, Nq=128, Nk=16384, D=128), -11),
+])
+def test_host_validation_decode_noalloc(over, code):
+    """attn_decode_noalloc checks its arguments like attn_decode and refuses, on the host and
+    before touching a device, a call whose split partials exceed its static scratch."""
+    a = dict(DECODE_OK)
+    a.update(over)
+    rc = binding.attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"],
+                                     a["Nk"], a["D"], a["scale"], a["causal"], a["key_lens"], a["dtype"],
+                                     a["stream"])
+    assert rc == code
+
+
+def test_decode_noalloc_scratch_limit_matches_header():
+    text = open(os.path.join(INCLUDE, "attn_fwd.h")).read()
+    m = re.search(r"#define ATTN_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 16 << 20
+    # just under and just over the limit: Nq queries per (b, h), 1024 split workgroups
+    for nq, want in ((31, 0), (32, -11)):
+        need = binding.attn_decode_workspace_size(1, 32, nq, 16384, 128, 2)
+        rc = binding.attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 32, nq, 16384, 128, 0.1, 1, None, 2, None) \
+            if want else None
+        if want:
+            assert need > 16 << 20 and rc == want
+        else:
+            assert need <= 16 << 20

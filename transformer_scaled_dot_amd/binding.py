@@ -1,8 +1,8 @@
 """Python binding of the C ABI in include/attn_fwd.h and include/attn_bwd.h (argument
 marshalling only).
 
-`attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size`, `attn_bwd`,
-`attn_bwd_window`, `attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one
+`attn_fwd`, `attn_fwd_window`, `attn_decode`, `attn_decode_workspace_size`, `attn_decode_noalloc`,
+`attn_bwd`, `attn_bwd_window`, `attn_bwd_workspace_size` and `attn_status_str` mirror the C entry points one
 to one (raw device pointers, sizes, a stream handle).  `fwd`, `decode` and `bwd` are the tensor-level
 conveniences: they check the tensors on the host, allocate the outputs (and workspaces) with
 torch on the current stream and call the matching entry point; `attention` joins the forward
@@ -24,9 +24,9 @@ ATTN_OK = 0
 STATUS = {
     0: "ATTN_OK", -1: "ATTN_ERR_NULL", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_HEAD_DIM",
     -4: "ATTN_ERR_DTYPE", -5: "ATTN_ERR_SCALE", -6: "ATTN_ERR_LAUNCH", -7: "ATTN_ERR_FLAG",
-    -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE",
+    -8: "ATTN_ERR_ALIGN", -9: "ATTN_ERR_WINDOW", -10: "ATTN_ERR_WORKSPACE", -11: "ATTN_ERR_SCRATCH",
 }
-EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_window", "attn_decode", "attn_decode_workspace_size", "attn_decode_noalloc",
            "attn_bwd", "attn_bwd_window", "attn_bwd_workspace_size", "attn_status_str")
 
 _lib = None
@@ -65,6 +65,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
         ctypes.c_void_p,
+    ]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
     ]
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
@@ -110,6 +116,12 @@ def attn_decode(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype
     """The C entry point for queries at the end of a KV cache (key split + merge)."""
     return load_library().attn_decode(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens,
                                       dtype, workspace, workspace_bytes, stream)
+
+
+def attn_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, stream) -> int:
+    """The C entry point of attn_decode with the library's static scratch (no workspace)."""
+    return load_library().attn_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens,
+                                              dtype, stream)
 
 
 def attn_decode_workspace_size(B, H, Nq, Nk, D, dtype) -> int:

@@ -2,6 +2,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include <attn_fwd.h>
 #include "attn_common.h"
 
@@ -120,18 +122,12 @@ extern "C" size_t attn_decode_workspace_size(int B, int H, int Nq, int Nk, int D
     return decode_plan(B, H, Nq, Nk, D, dtype).workspace_bytes;
 }
 
-extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int Nq, int Nk, int D, float scale, int causal,
-                           const int32_t* key_lens, int dtype, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-    attn::Params p;
-    const int rc = prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, p);
-    if (rc != ATTN_OK) return rc;
-    p.causal_br = 1;  // the queries are the last Nq positions of each cached sequence
-    const DecodePlan plan = decode_plan(B, H, Nq, Nk, D, dtype);
-    hipStream_t s = (hipStream_t)stream;
-    if (plan.n_splits == 1) return launch(p, dtype, D, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+namespace {
 
+// attn_decode's work after its argument checks, with the split partials in `workspace`.
+int decode_run(attn::Params& p, const DecodePlan& plan, int B, int H, int Nq, int D, int dtype,
+               void* workspace, size_t workspace_bytes, hipStream_t s) {
+    if (plan.n_splits == 1) return launch(p, dtype, D, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
     if (!workspace) return ATTN_ERR_NULL;
     if (((uintptr_t)workspace & 15) != 0) return ATTN_ERR_ALIGN;
     if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE;
@@ -144,6 +140,65 @@ extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o,
     p.lse_part = p.o_part + (size_t)plan.n_splits * B * H * Nq * D;
     if (launch(p, dtype, D, s) != hipSuccess) return ATTN_ERR_LAUNCH;
     return attn_launch_merge(p, dtype, D, s) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int Nq, int Nk, int D, float scale, int causal,
+                           const int32_t* key_lens, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    attn::Params p;
+    const int rc = prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, p);
+    if (rc != ATTN_OK) return rc;
+    p.causal_br = 1;  // the queries are the last Nq positions of each cached sequence
+    const DecodePlan plan = decode_plan(B, H, Nq, Nk, D, dtype);
+    return decode_run(p, plan, B, H, Nq, D, dtype, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+// ---- attn_decode without a caller workspace: the split partials live in `scratch`, a
+// file-scope device array of ATTN_DECODE_SCRATCH_BYTES.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device id, once looked up
+
+// The current device's copy of `scratch`, looked up on the first call on that device.
+// Returns nullptr if the device id is out of range or the lookup fails.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int H, int Nq, int Nk, int D, float scale, int causal,
+                                   const int32_t* key_lens, int dtype, void* stream) {
+    attn::Params p;
+    const int rc = prepare(q, k, v, o, lse, B, H, Nq, Nk, D, scale, causal, key_lens, dtype, p);
+    if (rc != ATTN_OK) return rc;
+    p.causal_br = 1;
+    const DecodePlan plan = decode_plan(B, H, Nq, Nk, D, dtype);
+    if (plan.workspace_bytes > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (plan.n_splits > 1 && !(ws = scratch_on_current_device())) return ATTN_ERR_LAUNCH;
+    // every split writes all of its rows' partials (O = 0, LSE = -inf where it sees no key)
+    // before the merge reads them, so nothing left by an earlier call needs clearing
+    return decode_run(p, plan, B, H, Nq, D, dtype, ws, ATTN_DECODE_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -165,7 +220,10 @@ extern "C" const char* attn_status_str(int status) {
         case ATTN_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
         case ATTN_ERR_ALIGN: return "q, k, v, o and lse must be 16-byte aligned, key_lens 4-byte aligned";
         case ATTN_ERR_WINDOW: return "window must be -1 (no band) or >= 0";
-        case ATTN_ERR_WORKSPACE: return "workspace_bytes is below attn_decode_workspace_size()";
+        case ATTN_ERR_WORKSPACE: return "workspace_bytes is below the *_workspace_size() query";
+        case ATTN_ERR_SCRATCH:
+            return "attn_decode_noalloc: the call needs more than the library's static scratch "
+                   "(ATTN_DECODE_SCRATCH_BYTES); use attn_decode with a workspace";
         default: return "unknown status";
     }
 }
