@@ -8,7 +8,8 @@
 // wave w taking key tiles w, w + NW, ...  Each wave keeps its own running max, sum and output; at
 // the end the waves' partial states of a row are combined by the log-sum-exp rule (rescale each
 // to the common max, add the sums and the outputs), the same rule the split-K merge applies
-// across workgroups.  K and V rows are read from LDS as broadcasts.  The key splits of the
+// across workgroups (here in a tree, log2 of the wave count rounds).  K and V rows are read from
+// LDS as broadcasts.  The key splits of the
 // matrix-core kernel apply here too (partial results for the merge kernel).
 #include "attn_common.h"
 
@@ -26,9 +27,8 @@ template <int D>
 __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn::Params p) {
     constexpr int NWF = waves_f32<D>();
     __shared__ float qs[BMF][D + 1];
-    __shared__ float kv[NWF][2][BNF][D];  // each wave's K and V tile; the merge reuses it
+    __shared__ float kv[NWF][2][BNF][D];  // each wave's K and V tile; the combine reuses it
     __shared__ float part_m[NWF][BMF], part_l[NWF][BMF];
-    static_assert(NWF * 2 * BNF * D >= BMF * (D + 1), "merge buffer does not fit");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -187,17 +187,30 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
 #pragma unroll
     for (int w = 0; w < NWF; ++w) l_all += part_l[w][lane] * __builtin_amdgcn_exp2f(part_m[w][lane] - m_ref);
     const float wgt = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float (*const os)[D + 1] = reinterpret_cast<float (*)[D + 1]>(&kv[0][0][0][0]);
-    // waves NWF-1 .. 1 add their weighted outputs into os in turn; wave 0 adds its own and stores
-    for (int w = NWF - 1; w >= 1; --w) {
-        if (wave == w) {
-            if (w == NWF - 1) {
+    // Tree combine of the weighted outputs: in each round the upper half of the remaining waves
+    // writes its output to a slot of the LDS the key loop no longer reads (the K/V tiles, then
+    // the Q tile) and the lower half adds it in: log2(NWF) rounds instead of NWF - 1 in turn.
+    // The order of the additions is fixed, so results are the same on every run.
+    constexpr int SLOT = BMF * (D + 1);                                    // floats per slot
+    constexpr int KV_SLOTS = (int)(sizeof(kv) / sizeof(float)) / SLOT;
+    constexpr int Q_SLOTS = (int)(sizeof(qs) / sizeof(float)) / SLOT;
+    static_assert(KV_SLOTS + Q_SLOTS >= NWF / 2, "not enough LDS for the tree combine");
+    auto slot = [&](const int i) -> float* {
+        return i < KV_SLOTS ? &kv[0][0][0][0] + i * SLOT : &qs[0][0] + (i - KV_SLOTS) * SLOT;
+    };
 #pragma unroll
-                for (int d = 0; d < D; ++d) os[lane][d] = o[d] * wgt;
-            } else {
+    for (int d = 0; d < D; ++d) o[d] *= wgt;
+    for (int half = NWF / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
+            float* dst = slot(wave - half) + lane * (D + 1);
 #pragma unroll
-                for (int d = 0; d < D; ++d) os[lane][d] += o[d] * wgt;
-            }
+            for (int d = 0; d < D; ++d) dst[d] = o[d];
+        }
+        __syncthreads();
+        if (wave < half) {
+            const float* src = slot(wave) + lane * (D + 1);
+#pragma unroll
+            for (int d = 0; d < D; ++d) o[d] += src[d];
         }
         __syncthreads();
     }
@@ -210,8 +223,7 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
         float* lg = p.n_splits > 1 ? p.lse_part : p.lse;
 #pragma unroll
         for (int d = 0; d < D; d += 4)
-            *(float4*)(og + d) = make_float4((os[lane][d] + o[d] * wgt) * inv, (os[lane][d + 1] + o[d + 1] * wgt) * inv,
-                                             (os[lane][d + 2] + o[d + 2] * wgt) * inv, (os[lane][d + 3] + o[d + 3] * wgt) * inv);
+            *(float4*)(og + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
         lg[row] = l_all > 0.f ? (m_all + __builtin_amdgcn_logf(l_all)) * attn::kLn2 : -INFINITY;
     }
 }
