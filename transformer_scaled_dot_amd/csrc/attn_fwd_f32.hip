@@ -2,20 +2,20 @@
 //
 // Same tiled loop as the matrix-core kernel (per Q tile, stream K/V tiles through LDS, online
 // softmax, never store S), but on the vector ALUs: fp32 MFMA would change nothing in the
-// precision and this path serves small fp32 problems.  One query row per lane; the NW waves of
-// a workgroup (eight for D = 64, four for D = 128) share the 64-row Q tile (in LDS, with a padded
-// row stride so that the 64 lanes reading one column hit 64 different banks) and split its keys,
-// wave w taking key tiles w, w + NW, ...  Each wave keeps its own running max, sum and output; at
-// the end the waves' partial states of a row are combined by the log-sum-exp rule (rescale each
-// to the common max, add the sums and the outputs), the same rule the split-K merge applies
-// across workgroups (here in a tree, log2 of the wave count rounds).  K and V rows are read from
-// LDS as broadcasts.  The key splits of the
+// precision and this path serves small fp32 problems.  Two lanes per query row, each owning half
+// of the head dimension; the NW waves of a workgroup (eight for D = 64, four for D = 128) share
+// the 32-row Q tile (in LDS, with a padded row stride so that the 64 lanes reading one column
+// slice hit 64 different banks) and split its keys, wave w taking key tiles w, w + NW, ...  Each
+// wave keeps its own running max, sum and output; at the end the waves' partial states of a row
+// are combined by the log-sum-exp rule (rescale each to the common max, add the sums and the
+// outputs), the same rule the split-K merge applies across workgroups (here in a tree, log2 of
+// the wave count rounds).  K and V rows are read from LDS as broadcasts.  The key splits of the
 // matrix-core kernel apply here too (partial results for the merge kernel).
 #include "attn_common.h"
 
 namespace {
 
-constexpr int BMF = 64;  // query rows per workgroup (one per lane)
+constexpr int BMF = 32;  // query rows per workgroup
 constexpr int BNF = 16;  // keys per K/V tile
 // waves per workgroup, each on every NW-th key tile (LDS: the Q tile plus one K and V tile per wave)
 template <int D>
@@ -23,15 +23,22 @@ constexpr int waves_f32() { return D == 64 ? 8 : 4; }
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// Two lanes per query row: lane (r, h) = (lane & 31, lane >> 5) owns row q0 + r and the columns
+// [h D/2, (h + 1) D/2) of Q and O.  A score is the sum of the two lanes' half dot products (one
+// v_permlane32_swap and one add), after which both lanes hold it and run the same softmax; each
+// then accumulates its half of the output.  Against one lane per row this halves the vector work
+// per row and lane and puts each row tile on twice as many workgroups (32 rows instead of 64).
 template <int D>
-__global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn::Params p) {
+__global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn::Params p) {
     constexpr int NWF = waves_f32<D>();
+    constexpr int DH = D / 2;  // columns per lane
     __shared__ float qs[BMF][D + 1];
     __shared__ float kv[NWF][2][BNF][D];  // each wave's K and V tile; the combine reuses it
     __shared__ float part_m[NWF][BMF], part_l[NWF][BMF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+    const int r = lane & 31, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits, p.xcd_interleave));
     const int bh = bw.bh;
@@ -39,7 +46,7 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
     if (p.causal && !p.causal_br) qt = p.n_qtiles - 1 - qt;
     const int b = bh / p.H;
     const int q0 = qt * BMF;
-    const int qi = q0 + lane;
+    const int qi = q0 + r;
 
     const float* qg = (const float*)p.q + (size_t)bh * p.Nq * D;
     const float* kg = (const float*)p.k + (size_t)bh * p.Nk * D;
@@ -48,16 +55,17 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
 
     {
         // 16-byte loads, all in flight together; rows past Nq fall outside the buffer and read as 0
-        constexpr int L4 = BMF * D / 4 / (BMF * NWF);
+        constexpr int L4 = BMF * D / 4 / (64 * NWF);
+        static_assert(L4 >= 1 && L4 * 4 * 64 * NWF == BMF * D, "Q tile load shape");
         const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(qg + (size_t)q0 * D), 0, (p.Nq - q0) * D * 4, kBufferWord3);
         f32x4_t qx[L4];
 #pragma unroll
         for (int i = 0; i < L4; ++i)
-            qx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, (i * BMF * NWF + tid) * 16, 0, 0));
+            qx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, (i * 64 * NWF + tid) * 16, 0, 0));
 #pragma unroll
         for (int i = 0; i < L4; ++i) {
-            const int e = (i * BMF * NWF + tid) * 4, row = e / D, d = e % D;
+            const int e = (i * 64 * NWF + tid) * 4, row = e / D, d = e % D;
 #pragma unroll
             for (int c = 0; c < 4; ++c) qs[row][d + c] = qsign * qx[i][c];
         }
@@ -76,10 +84,11 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
     const float c2 = p.scale_log2;
     float (*const ks)[D] = kv[wave][0];
     float (*const vs)[D] = kv[wave][1];
+    const int c0 = h * DH;  // this lane's first column
 
-    float o[D];
+    float o[DH];
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] = 0.f;
+    for (int d = 0; d < DH; ++d) o[d] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
     // Round r: wave w takes tile r * NWF + w.  The barriers keep the waves in rounds, so a wave's
@@ -91,7 +100,7 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
         if (t < n_tiles) {
             // 16-byte loads, all in flight together; rows at or past the valid length fall
             // outside the buffer and read as zeros
-            constexpr int L4 = BNF * D / 4 / BMF;  // float4s per lane per tile
+            constexpr int L4 = BNF * D / 4 / 64;  // float4s per lane per tile
             const int bytes = (kv_valid - j0) * D * 4;
             const __amdgpu_buffer_rsrc_t krs =
                 __builtin_amdgcn_make_buffer_rsrc((void*)(kg + (size_t)j0 * D), 0, bytes, kBufferWord3);
@@ -100,30 +109,31 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
             f32x4_t kx[L4], vx[L4];
 #pragma unroll
             for (int i = 0; i < L4; ++i) {
-                kx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, (i * BMF + lane) * 16, 0, 0));
-                vx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (i * BMF + lane) * 16, 0, 0));
+                kx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, (i * 64 + lane) * 16, 0, 0));
+                vx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (i * 64 + lane) * 16, 0, 0));
             }
 #pragma unroll
             for (int i = 0; i < L4; ++i) {
-                *(f32x4_t*)(&ks[0][0] + (i * BMF + lane) * 4) = kx[i];
-                *(f32x4_t*)(&vs[0][0] + (i * BMF + lane) * 4) = vx[i];
+                *(f32x4_t*)(&ks[0][0] + (i * 64 + lane) * 4) = kx[i];
+                *(f32x4_t*)(&vs[0][0] + (i * 64 + lane) * 4) = vx[i];
             }
         }
         __syncthreads();
         if (t >= n_tiles) continue;
 
-        // S for the tile's 16 keys: 16 independent accumulators, K read as 4-wide broadcasts
+        // half dot products for the tile's 16 keys: 16 independent accumulators, K read as 4-wide
+        // broadcasts (the two halves of the wave read two addresses)
         float s[BNF];
 #pragma unroll
         for (int jj = 0; jj < BNF; ++jj) s[jj] = 0.f;
 #pragma unroll 2
-        for (int d = 0; d < D; d += 4) {
+        for (int d = 0; d < DH; d += 4) {
             // all 16 broadcasts of this 4-column slice are requested before the first FMA, so one
             // wave per SIMD pays the LDS latency once per slice, not once per key
             f32x4_t kq[BNF];
 #pragma unroll
-            for (int jj = 0; jj < BNF; ++jj) kq[jj] = *(const f32x4_t*)&ks[jj][d];
-            const float q0v = qs[lane][d], q1v = qs[lane][d + 1], q2v = qs[lane][d + 2], q3v = qs[lane][d + 3];
+            for (int jj = 0; jj < BNF; ++jj) kq[jj] = *(const f32x4_t*)&ks[jj][c0 + d];
+            const float q0v = qs[r][c0 + d], q1v = qs[r][c0 + d + 1], q2v = qs[r][c0 + d + 2], q3v = qs[r][c0 + d + 3];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < BNF; ++jj) {
@@ -132,6 +142,13 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
                 s[jj] = __builtin_fmaf(q2v, kq[jj][2], s[jj]);
                 s[jj] = __builtin_fmaf(q3v, kq[jj][3], s[jj]);
             }
+        }
+        // whole scores: the low half's sum plus the high half's, the same order in both lanes
+#pragma unroll
+        for (int jj = 0; jj < BNF; ++jj) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, s[jj]),
+                                                             __builtin_bit_cast(unsigned, s[jj]), false, false);
+            s[jj] = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
         }
         float mt = -INFINITY;
 #pragma unroll
@@ -152,11 +169,11 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
         l_run = l_run * alpha + ls;
         m_run = m_new;
 #pragma unroll
-        for (int d = 0; d < D; d += 4) {
+        for (int d = 0; d < DH; d += 4) {
             float a0 = o[d] * alpha, a1 = o[d + 1] * alpha, a2 = o[d + 2] * alpha, a3 = o[d + 3] * alpha;
             f32x4_t vv[BNF];  // as for K: the slice's 16 broadcasts first
 #pragma unroll
-            for (int jj = 0; jj < BNF; ++jj) vv[jj] = *(const f32x4_t*)&vs[jj][d];
+            for (int jj = 0; jj < BNF; ++jj) vv[jj] = *(const f32x4_t*)&vs[jj][c0 + d];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int jj = 0; jj < BNF; ++jj) {
@@ -174,18 +191,21 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
     }
 
     // Combine the waves' partial states of each row (base 2): M = max_w m_w, l = sum_w 2^(m_w - M) l_w,
-    // O = sum_w 2^(m_w - M) O_w.  A wave that saw no key of the row has m = -inf and weight 0.
+    // O = sum_w 2^(m_w - M) O_w.  A wave that saw no key of the row has m = -inf and weight 0.  Both
+    // lanes of a row hold the same m and l; the low one publishes them.
     __syncthreads();
-    part_m[wave][lane] = m_run;
-    part_l[wave][lane] = l_run;
+    if (h == 0) {
+        part_m[wave][r] = m_run;
+        part_l[wave][r] = l_run;
+    }
     __syncthreads();
-    float m_all = part_m[0][lane];
+    float m_all = part_m[0][r];
 #pragma unroll
-    for (int w = 1; w < NWF; ++w) m_all = fmaxf(m_all, part_m[w][lane]);
+    for (int w = 1; w < NWF; ++w) m_all = fmaxf(m_all, part_m[w][r]);
     const float m_ref = m_all == -INFINITY ? 0.f : m_all;
     float l_all = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWF; ++w) l_all += part_l[w][lane] * __builtin_amdgcn_exp2f(part_m[w][lane] - m_ref);
+    for (int w = 0; w < NWF; ++w) l_all += part_l[w][r] * __builtin_amdgcn_exp2f(part_m[w][r] - m_ref);
     const float wgt = __builtin_amdgcn_exp2f(m_run - m_ref);
     // Tree combine of the weighted outputs: in each round the upper half of the remaining waves
     // writes its output to a slot of the LDS the key loop no longer reads (the K/V tiles, then
@@ -199,18 +219,18 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
         return i < KV_SLOTS ? &kv[0][0][0][0] + i * SLOT : &qs[0][0] + (i - KV_SLOTS) * SLOT;
     };
 #pragma unroll
-    for (int d = 0; d < D; ++d) o[d] *= wgt;
+    for (int d = 0; d < DH; ++d) o[d] *= wgt;
     for (int half = NWF / 2; half >= 1; half >>= 1) {
         if (wave >= half && wave < 2 * half) {
-            float* dst = slot(wave - half) + lane * (D + 1);
+            float* dst = slot(wave - half) + r * (D + 1) + c0;
 #pragma unroll
-            for (int d = 0; d < D; ++d) dst[d] = o[d];
+            for (int d = 0; d < DH; ++d) dst[d] = o[d];
         }
         __syncthreads();
         if (wave < half) {
-            const float* src = slot(wave) + lane * (D + 1);
+            const float* src = slot(wave) + r * (D + 1) + c0;
 #pragma unroll
-            for (int d = 0; d < D; ++d) o[d] += src[d];
+            for (int d = 0; d < DH; ++d) o[d] += src[d];
         }
         __syncthreads();
     }
@@ -219,12 +239,12 @@ __global__ void __launch_bounds__(BMF * waves_f32<D>()) attn_fwd_f32_kernel(attn
         const float inv = l_all > 0.f ? 1.f / l_all : 0.f;
         const size_t row = p.n_splits > 1 ? ((size_t)bw.split * p.B * p.H + bh) * p.Nq + qi
                                           : (size_t)bh * p.Nq + qi;
-        float* og = (p.n_splits > 1 ? p.o_part : (float*)p.o) + row * D;
+        float* og = (p.n_splits > 1 ? p.o_part : (float*)p.o) + row * D + c0;
         float* lg = p.n_splits > 1 ? p.lse_part : p.lse;
 #pragma unroll
-        for (int d = 0; d < D; d += 4)
+        for (int d = 0; d < DH; d += 4)
             *(float4*)(og + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-        lg[row] = l_all > 0.f ? (m_all + __builtin_amdgcn_logf(l_all)) * attn::kLn2 : -INFINITY;
+        if (h == 0) lg[row] = l_all > 0.f ? (m_all + __builtin_amdgcn_logf(l_all)) * attn::kLn2 : -INFINITY;
     }
 }
 
@@ -232,7 +252,7 @@ template <int D>
 hipError_t launch_one(const attn::Params& p, hipStream_t stream) {
     attn::Params pc = p;
     void* args[] = {&pc};
-    return hipLaunchKernel((const void*)attn_fwd_f32_kernel<D>, dim3(p.n_blocks), dim3(BMF * waves_f32<D>()), args,
+    return hipLaunchKernel((const void*)attn_fwd_f32_kernel<D>, dim3(p.n_blocks), dim3(64 * waves_f32<D>()), args,
                            0, stream);
 }
 
