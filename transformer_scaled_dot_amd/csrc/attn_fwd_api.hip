@@ -106,12 +106,14 @@ extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void
     if (window < -1) return ATTN_ERR_WINDOW;
     // |i - j| < max(Nq, Nk) always holds: a band at least that wide is no band.
     p.window = window >= (Nq > Nk ? Nq : Nk) ? -1 : window;
-    // Causal Q tiles differ in length (longest first within a head): each XCD alternates between
-    // four heads so that the long tiles of all its heads start before the short ones (the last
-    // XCD slots would otherwise run a few long tiles alone; 4K causal: +4 to 8 %).  Banded and
-    // unmasked tiles are of equal length and read overlapping K/V, which one head at a time
-    // keeps in the XCD's L2.
-    if (causal && p.window < 0) p.xcd_interleave = 4;
+    // Causal Q tiles differ in length (longest first within a head): with up to 8K rows each XCD
+    // alternates between four heads so that the long tiles of all its heads start before the
+    // short ones (the last XCD slots would otherwise run a few long tiles alone; 4K causal: +4 to
+    // 8 %).  Longer heads already fill an XCD's slots with tiles of every length, and four heads'
+    // K/V streams at once no longer share its L2: at 16K the interleave was no faster and fetched
+    // 3.8x the bytes from beyond the L2.  Banded and unmasked tiles are of equal length and read
+    // overlapping K/V, which one head at a time keeps in the XCD's L2.
+    if (causal && p.window < 0 && Nq <= 8192) p.xcd_interleave = 4;
     return launch(p, dtype, D, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

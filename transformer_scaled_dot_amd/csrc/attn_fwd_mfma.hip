@@ -381,13 +381,12 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_mfma_kernel(attn::Params p) {
         for (int t = 0; t < DT; ++t)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                // accumulator registers 4a..4a+3 hold O[qi][32 t + 8 a + 4 g + 0..3]
-                u32x2_t w;
-                w[0] = (unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 0] * inv)) |
-                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 1] * inv)) << 16);
-                w[1] = (unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 2] * inv)) |
-                       ((unsigned)__builtin_bit_cast(unsigned short, (T)(oacc[t][4 * a + 3] * inv)) << 16);
-                *(u32x2_t*)(og + 32 * t + 8 * a + 4 * g) = w;
+                // accumulator registers 4a..4a+3 hold O[qi][32 t + 8 a + 4 g + 0..3]; a vector of
+                // T converts two values per instruction (scalar casts joined by shifts took three)
+                using T4 = T __attribute__((ext_vector_type(4)));
+                const T4 w = {(T)(oacc[t][4 * a + 0] * inv), (T)(oacc[t][4 * a + 1] * inv),
+                              (T)(oacc[t][4 * a + 2] * inv), (T)(oacc[t][4 * a + 3] * inv)};
+                *(T4*)(og + 32 * t + 8 * a + 4 * g) = w;
             }
         if (g == 0)
             p.lse[(size_t)bh * p.Nq + qi] =
