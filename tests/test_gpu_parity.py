@@ -107,6 +107,42 @@ def test_parity_every_row_longctx_16k(first_head, oracle_impl):
         _LONGCTX_RUN.clear()
 
 
+# ------------------------------------------------------------------ long sequences
+# More than 8K query rows at D = 128 (no band, no key split) run the 256-row, 8-wave workgroups;
+# everything else the 128-row, 4-wave ones.  Both give each wave the same 32 rows and the same
+# per-row arithmetic, so besides the oracle the 8-wave output must equal, bit for bit, that of a
+# call with a band of width max(Nq, Nk) - 1 (no key is outside it, but a band keeps the 4-wave
+# workgroups).
+LONG = [
+    # name, dtype, B, H, Nq, Nk, causal, key_lens
+    ("long_causal_ragged_bf16", "bf16", 1, 2, 8300, 8300, True, None),
+    ("long_causal_ragged_f16", "f16", 1, 2, 8300, 8300, True, None),
+    ("long_noncausal_lens_bf16", "bf16", 2, 1, 8200, 8200, False, [5000, 8200]),
+    ("long_causal_lens_f16", "f16", 2, 1, 8400, 8400, True, [8400, 3001]),
+    ("long_causal_nq_gt_nk_bf16", "bf16", 1, 1, 9000, 4000, True, None),
+    ("long_causal_nq_lt_nk_bf16", "bf16", 1, 1, 8500, 12000, True, None),
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[c[0] for c in LONG])
+def test_long_sequence_workgroups(case, oracle_impl):
+    name, dtype, B, H, Nq, Nk, causal, kl = case
+    log(f"[long] {name}")
+    w = inputs.Workload(name, dtype, B, H, Nq, Nk, 128, causal, kl is not None, 0.5, 1.0, 91)
+    x = inputs.make_inputs(w)
+    if kl is not None:
+        x["key_lens"] = np.array(kl, np.int32)
+    o, lse = run(x, dtype, causal)
+    o4, lse4 = run(x, dtype, causal, window=max(Nq, Nk) - 1)
+    assert torch.equal(o.view(torch.int16), o4.view(torch.int16)), f"{name}: O differs from the 4-wave launch"
+    assert torch.equal(lse, lse4), f"{name}: LSE differs from the 4-wave launch"
+    rows = sample_rows(w, 512, block_m=256)
+    ro, rl = oracle_impl.attn_rows(x["q"], x["k"], x["v"], dtype, float(x["scale"]), causal,
+                                   x["key_lens"], rows)
+    eo, el = compare(o, lse, ro, rl, dtype, name, rows=rows)
+    log(f"[long] {name}: {rows.size} rows, max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # name, B, H, Nq, Nk, D, causal, key_lens, scale
