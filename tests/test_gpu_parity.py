@@ -121,6 +121,10 @@ LONG = [
     ("long_causal_lens_f16", "f16", 2, 1, 8400, 8400, True, [8400, 3001]),
     ("long_causal_nq_gt_nk_bf16", "bf16", 1, 1, 9000, 4000, True, None),
     ("long_causal_nq_lt_nk_bf16", "bf16", 1, 1, 8500, 12000, True, None),
+    # either side of the switch: 8192 rows keep the 4-wave workgroups, 8193 take the 8-wave ones
+    # (whose last 256-row tile then holds a single row)
+    ("boundary_8192_bf16", "bf16", 1, 2, 8192, 8192, True, None),
+    ("boundary_8193_bf16", "bf16", 1, 2, 8193, 8193, True, None),
 ]
 
 
